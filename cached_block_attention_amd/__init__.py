@@ -1,0 +1,342 @@
+"""Block-diffusion attention over a cached prefix on AMD MI355X (gfx950).
+
+Thin Python binding of libblkattn.so (C ABI in include/blkattn.h). Every
+function here only marshals arguments: torch tensors supply device memory and
+the current HIP stream; all arithmetic runs in the library's HIP kernels. There
+is no CPU fallback: the functions raise if the library is missing or a tensor
+is not on the GPU.
+
+Tensors are [B, H, T, d] with a unit stride along d (head_dim):
+  q [B, Hq, Bq, d]; k_pre/v_pre [B, Hkv, P, d]; k_blk/v_blk [B, Hkv, Bq, d];
+  idx int32 [B, Hkv, n_keep] (contiguous); o [B, Hq, Bq, d] (dtype of q);
+  lse fp32 [B, Hq, Bq]; a partial is (o fp32 [B, Hq, Bq, d], m, l fp32 [B, Hq, Bq]).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import NamedTuple, Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libblkattn.so")
+
+F32 = 0
+BF16 = 1
+OP_FULL = 0
+OP_PREFIX_PARTIAL = 1
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_heads", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_len", ctypes.c_int32),
+        ("n_keep", ctypes.c_int32),
+        ("prefix_len", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64),
+        ("stride_t", ctypes.c_int64),
+    ]
+
+
+class PartialDesc(ctypes.Structure):
+    _fields_ = [("o", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p)]
+
+
+class Partial(NamedTuple):
+    """A partial online-softmax state: o (normalised), m (max score), l (sum)."""
+    o: "object"
+    m: "object"
+    l: "object"
+
+
+class BlkAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"blkattn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.POINTER
+
+
+def library() -> ctypes.CDLL:
+    """Load libblkattn.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python -c "
+                          "'import __graft_entry__; __graft_entry__.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pd, pt, pp = _P(Dims), _P(Tensor), _P(PartialDesc)
+    sig = {
+        "blkattn_full": (ctypes.c_int, [pd, pt, pt, pt, vp, pt, pt, pt, vp, vp, sz, vp]),
+        "blkattn_prefix_partial": (ctypes.c_int, [pd, pt, pt, pt, vp, pp, vp, sz, vp]),
+        "blkattn_block_partial": (ctypes.c_int, [pd, pt, pt, pt, pp, vp]),
+        "blkattn_merge": (ctypes.c_int, [pd, pp, pp, pt, vp, pp, vp]),
+        "blkattn_gather_prefix": (ctypes.c_int, [pd, pt, pt, vp, pt, pt, vp]),
+        "blkattn_workspace_bytes": (ctypes.c_size_t, [pd, ctypes.c_int]),
+        "blkattn_plan_splits": (ctypes.c_int, [pd, ctypes.c_int]),
+        "blkattn_set_kernel_events": (None, [vp, vp]),
+        "blkattn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "blkattn_last_error": (ctypes.c_char_p, []),
+        "blkattn_abi_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("blkattn runs on the GPU only: every tensor must be a CUDA/HIP tensor")
+
+
+def _tensor(t) -> Optional[Tensor]:
+    if t is None:
+        return None
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, H, T, d] tensor, got shape {tuple(t.shape)}")
+    if t.numel() == 0:
+        return Tensor(None, 0, 0, 0)
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the head_dim axis must have unit stride")
+    return Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _partial(p: Optional[Partial]) -> Optional[PartialDesc]:
+    if p is None:
+        return None
+    for x in p:
+        if not x.is_contiguous():
+            raise ValueError("partial tensors must be contiguous")
+    return PartialDesc(p.o.data_ptr(), p.m.data_ptr(), p.l.data_ptr())
+
+
+def _ref(x):
+    return ctypes.byref(x) if x is not None else None
+
+
+def _ptr(t) -> Optional[int]:
+    return t.data_ptr() if t is not None else None
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _raise(status: int):
+    if status != OK:
+        lib = library()
+        raise BlkAttnError(status, lib.blkattn_last_error().decode() or lib.blkattn_strerror(status).decode())
+
+
+def make_dims(q, kv_heads: int, prefix_len: int, n_keep: int = 0, scale: Optional[float] = None,
+              splits: int = 0) -> Dims:
+    B, Hq, Bq, d = q.shape
+    return Dims(B, Hq, kv_heads, d, Bq, n_keep, prefix_len, _dtype_code(q),
+                float(1.0 / math.sqrt(d) if scale is None else scale), splits, 0)
+
+
+def workspace_bytes(dims: Dims, op: int) -> int:
+    return int(library().blkattn_workspace_bytes(ctypes.byref(dims), op))
+
+
+def plan_splits(dims: Dims, op: int) -> int:
+    s = library().blkattn_plan_splits(ctypes.byref(dims), op)
+    if s < 0:
+        _raise(s)
+    return s
+
+
+def _workspace(dims: Dims, op: int, device, workspace):
+    torch = _torch()
+    need = workspace_bytes(dims, op)
+    if need == 0:
+        return None, 0
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def empty_partial(B: int, Hq: int, Bq: int, d: int, device) -> Partial:
+    torch = _torch()
+    return Partial(torch.empty(B, Hq, Bq, d, dtype=torch.float32, device=device),
+                   torch.empty(B, Hq, Bq, dtype=torch.float32, device=device),
+                   torch.empty(B, Hq, Bq, dtype=torch.float32, device=device))
+
+
+def set_kernel_events(start, stop):
+    """Record torch.cuda.Event `start`/`stop` around the next attention kernel."""
+    handles = []
+    for ev in (start, stop):
+        if ev is None:
+            handles.append(None)
+            continue
+        if not ev.cuda_event:          # torch creates the HIP event on first record
+            ev.record()
+        handles.append(ev.cuda_event)
+    library().blkattn_set_kernel_events(*handles)
+
+
+# ---------------------------------------------------------------------------
+# the five entry points
+# ---------------------------------------------------------------------------
+
+def blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=None, splits=0,
+                 workspace=None, stream=None):
+    """O (and LSE) of the block queries over [prefix (or its idx rows); block]."""
+    _check_gpu(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx)
+    n_keep = int(idx.shape[-1]) if idx is not None else 0
+    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    ws, nbytes = _workspace(dims, OP_FULL, q.device, workspace)
+    st = library().blkattn_full(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
+                                _ref(_tensor(v_pre)), _ptr(idx), _ref(_tensor(k_blk)),
+                                _ref(_tensor(v_blk)), _ref(_tensor(o)), _ptr(lse), _ptr(ws),
+                                nbytes, _stream(stream))
+    _raise(st)
+    return o, lse
+
+
+def blkattn_prefix_partial(q, k_pre, v_pre, out: Partial, idx=None, scale=None, splits=0,
+                           workspace=None, stream=None):
+    """Partial state of the block queries over the prefix (the FACache state)."""
+    _check_gpu(q, k_pre, v_pre, idx, *out)
+    n_keep = int(idx.shape[-1]) if idx is not None else 0
+    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    ws, nbytes = _workspace(dims, OP_PREFIX_PARTIAL, q.device, workspace)
+    st = library().blkattn_prefix_partial(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
+                                          _ref(_tensor(v_pre)), _ptr(idx), _ref(_partial(out)),
+                                          _ptr(ws), nbytes, _stream(stream))
+    _raise(st)
+    return out
+
+
+def blkattn_block_partial(q, k_blk, v_blk, out: Partial, scale=None, stream=None):
+    """Partial state of the block queries over the block's own keys (no mask)."""
+    _check_gpu(q, k_blk, v_blk, *out)
+    dims = make_dims(q, k_blk.shape[1], 0, 0, scale, 0)
+    st = library().blkattn_block_partial(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_blk)),
+                                         _ref(_tensor(v_blk)), _ref(_partial(out)), _stream(stream))
+    _raise(st)
+    return out
+
+
+def blkattn_merge(a: Partial, b: Partial, o=None, lse=None, ab: Optional[Partial] = None,
+                  dtype=None, stream=None):
+    """Log-sum-exp merge of two partials; writes O (dtype of `o`), LSE and/or `ab`."""
+    torch = _torch()
+    _check_gpu(*a, *b, o, lse, *(ab or ()))
+    B, Hq, Bq, d = a.o.shape
+    code = _dtype_code(o) if o is not None else (BF16 if dtype == torch.bfloat16 else F32)
+    dims = Dims(B, Hq, 1, d, Bq, 0, 0, code, 1.0, 0, 0)
+    st = library().blkattn_merge(ctypes.byref(dims), _ref(_partial(a)), _ref(_partial(b)),
+                                 _ref(_tensor(o)), _ptr(lse), _ref(_partial(ab)), _stream(stream))
+    _raise(st)
+    return o, lse, ab
+
+
+def blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=None):
+    """Bit copy of the retained prefix rows named by idx."""
+    _check_gpu(k_full, v_full, idx, k_out, v_out)
+    B, Hkv, P, d = k_full.shape
+    dims = Dims(B, Hkv, Hkv, d, 1, int(idx.shape[-1]), P, _dtype_code(k_full), 1.0, 0, 0)
+    st = library().blkattn_gather_prefix(ctypes.byref(dims), _ref(_tensor(k_full)), _ref(_tensor(v_full)),
+                                         _ptr(idx), _ref(_tensor(k_out)), _ref(_tensor(v_out)),
+                                         _stream(stream))
+    _raise(st)
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# allocating conveniences (device memory from torch, compute in the library)
+# ---------------------------------------------------------------------------
+
+def attention(q, k_pre, v_pre, k_blk, v_blk, idx=None, scale=None, splits=0, stream=None):
+    """Allocate O and LSE and run blkattn_full."""
+    torch = _torch()
+    B, Hq, Bq, d = q.shape
+    o = torch.empty(B, Hq, Bq, d, dtype=q.dtype, device=q.device)
+    lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device=q.device)
+    return blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx=idx, scale=scale, splits=splits,
+                        stream=stream)
+
+
+def prefix_partial(q, k_pre, v_pre, idx=None, scale=None, splits=0, stream=None) -> Partial:
+    B, Hq, Bq, d = q.shape
+    out = empty_partial(B, Hq, Bq, d, q.device)
+    return blkattn_prefix_partial(q, k_pre, v_pre, out, idx=idx, scale=scale, splits=splits, stream=stream)
+
+
+def block_partial(q, k_blk, v_blk, scale=None, stream=None) -> Partial:
+    B, Hq, Bq, d = q.shape
+    out = empty_partial(B, Hq, Bq, d, q.device)
+    return blkattn_block_partial(q, k_blk, v_blk, out, scale=scale, stream=stream)
+
+
+def merge(a: Partial, b: Partial, dtype=None, stream=None):
+    """Return (O in `dtype`, LSE) of two merged partials."""
+    torch = _torch()
+    dtype = dtype or torch.float32
+    B, Hq, Bq, d = a.o.shape
+    o = torch.empty(B, Hq, Bq, d, dtype=dtype, device=a.o.device)
+    lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device=a.o.device)
+    blkattn_merge(a, b, o=o, lse=lse, stream=stream)
+    return o, lse
+
+
+def gather_prefix(k_full, v_full, idx, stream=None):
+    torch = _torch()
+    B, Hkv, P, d = k_full.shape
+    n = int(idx.shape[-1])
+    k_out = torch.empty(B, Hkv, n, d, dtype=k_full.dtype, device=k_full.device)
+    v_out = torch.empty(B, Hkv, n, d, dtype=v_full.dtype, device=v_full.device)
+    return blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=stream)

@@ -1,0 +1,466 @@
+// Host side of libblkattn.so: argument validation, the key-split plan,
+// workspace layout and kernel launches behind the C ABI of include/blkattn.h.
+//
+// The library is stateless apart from a thread-local error message and the
+// thread-local one-shot measurement events; it never allocates, frees or
+// synchronises, and enqueues everything on the caller's stream.
+#include "blkattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace {
+
+using namespace blkattn;
+
+thread_local char g_err[512] = "";
+thread_local void* g_ev_start = nullptr;
+thread_local void* g_ev_stop = nullptr;
+
+// Workgroups the automatic plan aims for: two per compute unit of a 256-CU
+// MI355X. A fixed target keeps the plan (and so the bits of the result) a
+// function of the dims alone.
+constexpr int64_t kTargetWorkgroups = 512;
+// Each key split keeps at least this many 64-key tiles, which bounds the
+// split-partial traffic (d+2 fp32 per row per split) relative to the K/V
+// stream.
+constexpr int64_t kMinTilesPerSplit = 4;
+constexpr size_t kWsAlign = 256;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BLKATTN_OK;
+}
+
+int elt_bytes(int dtype) { return dtype == BLKATTN_F32 ? 4 : 2; }
+
+int check_dims(const blkattn_dims* d) {
+  if (d == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "dims is NULL");
+  if (d->reserved != 0) return fail(BLKATTN_ERR_INVALID_ARG, "dims.reserved must be 0");
+  if (d->batch < 0 || d->q_heads < 0 || d->block_len < 0 || d->prefix_len < 0 || d->n_keep < 0 ||
+      d->splits < 0)
+    return fail(BLKATTN_ERR_INVALID_ARG, "negative size in dims");
+  if (d->kv_heads <= 0) return fail(BLKATTN_ERR_INVALID_ARG, "kv_heads must be > 0");
+  if (d->q_heads % d->kv_heads != 0)
+    return fail(BLKATTN_ERR_INVALID_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", d->q_heads,
+                d->kv_heads);
+  if (d->dtype != BLKATTN_F32 && d->dtype != BLKATTN_BF16)
+    return fail(BLKATTN_ERR_UNSUPPORTED, "dtype %d is not supported", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(BLKATTN_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+  if (!(d->scale > 0.0f) || !std::isfinite(d->scale))
+    return fail(BLKATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return BLKATTN_OK;
+}
+
+// A [B, H, T, d] tensor with `rows` rows; with rows == 0 it may be absent.
+int check_tensor(const blkattn_tensor* t, const char* name, int eb, int64_t rows) {
+  if (rows == 0 && (t == nullptr || t->data == nullptr)) return BLKATTN_OK;
+  if (t == nullptr || t->data == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_t < 0)
+    return fail(BLKATTN_ERR_INVALID_ARG, "%s has a negative stride", name);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "%s data pointer is not 16-byte aligned", name);
+  if ((t->stride_b * eb) % 16 != 0 || (t->stride_h * eb) % 16 != 0 || (t->stride_t * eb) % 16 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "%s strides are not multiples of 16 bytes", name);
+  return BLKATTN_OK;
+}
+
+int check_partial(const blkattn_partial* p, const char* name, int64_t rows) {
+  if (rows == 0 && p == nullptr) return BLKATTN_OK;
+  if (p == nullptr || p->o == nullptr || p->m == nullptr || p->l == nullptr)
+    return fail(BLKATTN_ERR_INVALID_ARG, "%s (or one of its o, m, l) is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p->o) % 16 != 0 || reinterpret_cast<uintptr_t>(p->m) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(p->l) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "%s.o must be 16-byte aligned (m, l 4-byte)", name);
+  return BLKATTN_OK;
+}
+
+struct Plan {
+  int waves = 1;        // waves per workgroup (bf16 kernel)
+  int rows_per_wg = 0;  // packed rows per workgroup
+  int row_chunks = 1;
+  int tile_keys = 64;   // keys per staged tile of the chosen kernel
+  int tiles = 0;        // tiles of tile_keys over the key sequence
+  int splits = 1;
+};
+
+Plan make_plan(const blkattn_dims* d, int64_t n_keys) {
+  Plan pl;
+  const int64_t G = d->q_heads / d->kv_heads;
+  const int64_t R = G * d->block_len;
+  int64_t base;
+  if (d->dtype == BLKATTN_F32) {
+    pl.tile_keys = 32;
+    base = (int64_t)d->batch * d->q_heads;
+  } else {
+    if (R <= 32) {
+      pl.waves = 1;
+      pl.row_chunks = 1;
+    } else {
+      pl.row_chunks = (int)((R + 255) / 256);
+      pl.waves = (int)((R + 32 * pl.row_chunks - 1) / (32 * pl.row_chunks));
+    }
+    pl.rows_per_wg = 32 * pl.waves;
+    pl.tile_keys = bf16_tile_keys(pl.waves);
+    base = (int64_t)d->batch * d->kv_heads * pl.row_chunks;
+  }
+  pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
+  const int64_t tiles64 = (n_keys + 63) / 64;
+  int64_t s;
+  if (d->splits > 0) {
+    s = d->splits;
+  } else {
+    s = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
+    const int64_t cap = tiles64 / kMinTilesPerSplit;
+    if (s > cap) s = cap;
+  }
+  if (s > tiles64) s = tiles64;
+  if (s > pl.tiles) s = pl.tiles;
+  if (s < 1) s = 1;
+  pl.splits = (int)s;
+  return pl;
+}
+
+struct WsLayout {
+  size_t o = 0, m = 0, l = 0, total = 0;
+};
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+WsLayout ws_layout(const blkattn_dims* d, int splits) {
+  WsLayout w;
+  if (splits <= 1) return w;
+  const size_t rows = (size_t)d->batch * d->q_heads * d->block_len;
+  w.o = 0;
+  w.m = align_up(w.o + (size_t)splits * rows * d->head_dim * sizeof(float));
+  w.l = align_up(w.m + (size_t)splits * rows * sizeof(float));
+  w.total = align_up(w.l + (size_t)splits * rows * sizeof(float));
+  return w;
+}
+
+int64_t prefix_keys(const blkattn_dims* d, const int32_t* idx) { return idx ? d->n_keep : d->prefix_len; }
+
+void fill_keys(KeySeq& ks, const blkattn_dims* d, const blkattn_tensor* k_pre, const blkattn_tensor* v_pre,
+               const int32_t* idx, const blkattn_tensor* k_blk, const blkattn_tensor* v_blk, int64_t n_pre,
+               int32_t n_blk) {
+  ks = KeySeq{};
+  ks.n_pre = n_pre;
+  ks.n_blk = n_blk;
+  ks.p_rows = d->prefix_len;
+  ks.idx = idx;
+  if (n_pre > 0) {
+    ks.k_pre = k_pre->data;
+    ks.kp_sb = k_pre->stride_b, ks.kp_sh = k_pre->stride_h, ks.kp_st = k_pre->stride_t;
+    ks.v_pre = v_pre->data;
+    ks.vp_sb = v_pre->stride_b, ks.vp_sh = v_pre->stride_h, ks.vp_st = v_pre->stride_t;
+  }
+  if (n_blk > 0) {
+    ks.k_blk = k_blk->data;
+    ks.kb_sb = k_blk->stride_b, ks.kb_sh = k_blk->stride_h, ks.kb_st = k_blk->stride_t;
+    ks.v_blk = v_blk->data;
+    ks.vb_sb = v_blk->stride_b, ks.vb_sh = v_blk->stride_h, ks.vb_st = v_blk->stride_t;
+  }
+}
+
+AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Plan& pl) {
+  AttnParams p{};
+  p.batch = d->batch;
+  p.q_heads = d->q_heads;
+  p.kv_heads = d->kv_heads;
+  p.group = d->q_heads / d->kv_heads;
+  p.head_dim = d->head_dim;
+  p.block_len = d->block_len;
+  p.q = q->data;
+  p.q_sb = q->stride_b, p.q_sh = q->stride_h, p.q_st = q->stride_t;
+  p.scale = d->scale;
+  p.scale_log2 = (float)((double)d->scale * 1.4426950408889634);
+  p.splits = pl.splits;
+  p.tiles = pl.tiles;
+  p.rows_per_wg = pl.rows_per_wg;
+  p.row_chunks = pl.row_chunks;
+  return p;
+}
+
+int launch_attn(const blkattn_dims* d, const AttnParams& p, const Plan& pl, hipStream_t stream) {
+  if (g_ev_start) hipEventRecord((hipEvent_t)g_ev_start, stream);
+  hipError_t e = d->dtype == BLKATTN_F32 ? launch_attn_f32(p, stream) : launch_attn_bf16(p, pl.waves, stream);
+  if (g_ev_stop) hipEventRecord((hipEvent_t)g_ev_stop, stream);
+  g_ev_start = g_ev_stop = nullptr;
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+  return BLKATTN_OK;
+}
+
+int check_idx(const blkattn_dims* d, const int32_t* idx) {
+  if (idx == nullptr) {
+    if (d->n_keep != 0) return fail(BLKATTN_ERR_INVALID_ARG, "n_keep is set but idx is NULL");
+    return BLKATTN_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(idx) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "idx is not 4-byte aligned");
+  if (d->n_keep > 0 && d->prefix_len == 0)
+    return fail(BLKATTN_ERR_INVALID_ARG, "n_keep > 0 with an empty prefix to index");
+  return BLKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int blkattn_abi_version(void) { return BLKATTN_ABI_VERSION; }
+
+const char* blkattn_last_error(void) { return g_err; }
+
+const char* blkattn_strerror(int status) {
+  switch (status) {
+    case BLKATTN_OK: return "ok";
+    case BLKATTN_ERR_INVALID_ARG: return "invalid argument";
+    case BLKATTN_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+    case BLKATTN_ERR_MISALIGNED: return "pointer or stride not 16-byte aligned";
+    case BLKATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case BLKATTN_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+void blkattn_set_kernel_events(void* start, void* stop) {
+  g_ev_start = start;
+  g_ev_stop = stop;
+}
+
+int blkattn_plan_splits(const blkattn_dims* d, int op) {
+  int st = check_dims(d);
+  if (st != BLKATTN_OK) return st;
+  if (op != BLKATTN_OP_FULL && op != BLKATTN_OP_PREFIX_PARTIAL)
+    return fail(BLKATTN_ERR_INVALID_ARG, "unknown op %d", op);
+  const int64_t n_pre = d->n_keep > 0 ? d->n_keep : d->prefix_len;
+  const int64_t n_keys = n_pre + (op == BLKATTN_OP_FULL ? d->block_len : 0);
+  return make_plan(d, n_keys).splits;
+}
+
+size_t blkattn_workspace_bytes(const blkattn_dims* d, int op) {
+  const int s = blkattn_plan_splits(d, op);
+  if (s < 1) return 0;
+  return ws_layout(d, s).total;
+}
+
+int blkattn_full(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                 const blkattn_tensor* v_pre, const int32_t* idx, const blkattn_tensor* k_blk,
+                 const blkattn_tensor* v_blk, const blkattn_tensor* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  const int64_t n_pre = prefix_keys(d, idx);
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if ((st = check_tensor(k_pre, "k_pre", eb, n_pre))) return st;
+  if ((st = check_tensor(v_pre, "v_pre", eb, n_pre))) return st;
+  if ((st = check_idx(d, idx))) return st;
+  if ((st = check_tensor(k_blk, "k_blk", eb, 1))) return st;
+  if ((st = check_tensor(v_blk, "v_blk", eb, 1))) return st;
+  if ((st = check_tensor(o, "o", eb, 1))) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  const int64_t n_keys = n_pre + d->block_len;
+  const Plan pl = make_plan(d, n_keys);
+  const WsLayout wl = ws_layout(d, pl.splits);
+  if (wl.total > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  AttnParams p = attn_params(d, q, pl);
+  fill_keys(p.keys, d, k_pre, v_pre, idx, k_blk, v_blk, n_pre, d->block_len);
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  if (pl.splits == 1) {
+    p.out.mode = kOutFinal;
+    p.out.o = o->data;
+    p.out.o_sb = o->stride_b, p.out.o_sh = o->stride_h, p.out.o_st = o->stride_t;
+    p.out.lse = lse;
+    if ((st = launch_attn(d, p, pl, s))) return st;
+    return ok();
+  }
+  char* ws = (char*)workspace;
+  p.out.mode = kOutPartial;
+  p.out.po = (float*)(ws + wl.o);
+  p.out.pm = (float*)(ws + wl.m);
+  p.out.pl = (float*)(ws + wl.l);
+  p.out.split_rows = rows;
+  if ((st = launch_attn(d, p, pl, s))) return st;
+  MergeParams mp{};
+  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
+  mp.nsrc = pl.splits;
+  mp.strided = 1;
+  mp.split_rows = rows;
+  mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
+  mp.out_dtype = d->dtype;
+  mp.o_final = o->data;
+  mp.o_sb = o->stride_b, mp.o_sh = o->stride_h, mp.o_st = o->stride_t;
+  mp.lse = lse;
+  hipError_t e = launch_merge(mp, s);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int blkattn_prefix_partial(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                           const blkattn_tensor* v_pre, const int32_t* idx, const blkattn_partial* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  const int64_t n_pre = prefix_keys(d, idx);
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if ((st = check_tensor(k_pre, "k_pre", eb, n_pre))) return st;
+  if ((st = check_tensor(v_pre, "v_pre", eb, n_pre))) return st;
+  if ((st = check_idx(d, idx))) return st;
+  if ((st = check_partial(out, "out", rows))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (n_pre == 0) {
+    hipError_t e = launch_fill_empty(out->o, out->m, out->l, rows, d->head_dim, s);
+    if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "fill kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  const Plan pl = make_plan(d, n_pre);
+  const WsLayout wl = ws_layout(d, pl.splits);
+  if (wl.total > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  }
+  AttnParams p = attn_params(d, q, pl);
+  fill_keys(p.keys, d, k_pre, v_pre, idx, nullptr, nullptr, n_pre, 0);
+  p.out.mode = kOutPartial;
+  if (pl.splits == 1) {
+    p.out.po = out->o, p.out.pm = out->m, p.out.pl = out->l;
+    p.out.split_rows = rows;
+    if ((st = launch_attn(d, p, pl, s))) return st;
+    return ok();
+  }
+  char* ws = (char*)workspace;
+  p.out.po = (float*)(ws + wl.o);
+  p.out.pm = (float*)(ws + wl.m);
+  p.out.pl = (float*)(ws + wl.l);
+  p.out.split_rows = rows;
+  if ((st = launch_attn(d, p, pl, s))) return st;
+  MergeParams mp{};
+  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
+  mp.nsrc = pl.splits;
+  mp.strided = 1;
+  mp.split_rows = rows;
+  mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
+  mp.out_dtype = d->dtype;
+  mp.out_o = out->o, mp.out_m = out->m, mp.out_l = out->l;
+  hipError_t e = launch_merge(mp, s);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int blkattn_block_partial(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_blk,
+                          const blkattn_tensor* v_blk, const blkattn_partial* out, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if ((st = check_tensor(k_blk, "k_blk", eb, 1))) return st;
+  if ((st = check_tensor(v_blk, "v_blk", eb, 1))) return st;
+  if ((st = check_partial(out, "out", rows))) return st;
+  blkattn_dims d1 = *d;
+  d1.splits = 1;  // no workspace on this path: one split over the block's keys
+  const Plan pl = make_plan(&d1, d->block_len);
+  AttnParams p = attn_params(&d1, q, pl);
+  fill_keys(p.keys, &d1, nullptr, nullptr, nullptr, k_blk, v_blk, 0, d->block_len);
+  p.out.mode = kOutPartial;
+  p.out.po = out->o, p.out.pm = out->m, p.out.pl = out->l;
+  p.out.split_rows = rows;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->dtype == BLKATTN_F32) {
+    hipError_t e = launch_attn_f32(p, s);
+    if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+  } else {
+    hipError_t e = launch_attn_bf16(p, pl.waves, s);
+    if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+int blkattn_merge(const blkattn_dims* d, const blkattn_partial* a, const blkattn_partial* b,
+                  const blkattn_tensor* o, float* lse, const blkattn_partial* ab, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  if ((st = check_partial(a, "a", rows))) return st;
+  if ((st = check_partial(b, "b", rows))) return st;
+  if (o != nullptr && (st = check_tensor(o, "o", elt_bytes(d->dtype), 1))) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  if (ab != nullptr && (st = check_partial(ab, "ab", rows))) return st;
+  if (o == nullptr && lse == nullptr && ab == nullptr) return ok();
+  MergeParams mp{};
+  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
+  mp.nsrc = 2;
+  mp.strided = 0;
+  mp.src_o[0] = a->o, mp.src_m[0] = a->m, mp.src_l[0] = a->l;
+  mp.src_o[1] = b->o, mp.src_m[1] = b->m, mp.src_l[1] = b->l;
+  mp.out_dtype = d->dtype;
+  if (o != nullptr) {
+    mp.o_final = o->data;
+    mp.o_sb = o->stride_b, mp.o_sh = o->stride_h, mp.o_st = o->stride_t;
+  }
+  mp.lse = lse;
+  if (ab != nullptr) mp.out_o = ab->o, mp.out_m = ab->m, mp.out_l = ab->l;
+  hipError_t e = launch_merge(mp, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int blkattn_gather_prefix(const blkattn_dims* d, const blkattn_tensor* k_full, const blkattn_tensor* v_full,
+                          const int32_t* idx, const blkattn_tensor* k_out, const blkattn_tensor* v_out,
+                          void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  if (d->batch == 0 || d->n_keep == 0) return ok();
+  if (idx == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "idx is NULL");
+  if ((st = check_idx(d, idx))) return st;
+  if ((st = check_tensor(k_full, "k_full", eb, 1))) return st;
+  if ((st = check_tensor(v_full, "v_full", eb, 1))) return st;
+  if ((st = check_tensor(k_out, "k_out", eb, 1))) return st;
+  if ((st = check_tensor(v_out, "v_out", eb, 1))) return st;
+  GatherParams gp{};
+  gp.batch = d->batch, gp.kv_heads = d->kv_heads, gp.head_dim = d->head_dim, gp.elt_bytes = eb;
+  gp.p_rows = d->prefix_len, gp.n_keep = d->n_keep, gp.idx = idx;
+  gp.k_full = k_full->data, gp.kf_sb = k_full->stride_b, gp.kf_sh = k_full->stride_h, gp.kf_st = k_full->stride_t;
+  gp.v_full = v_full->data, gp.vf_sb = v_full->stride_b, gp.vf_sh = v_full->stride_h, gp.vf_st = v_full->stride_t;
+  gp.k_out = k_out->data, gp.ko_sb = k_out->stride_b, gp.ko_sh = k_out->stride_h, gp.ko_st = k_out->stride_t;
+  gp.v_out = v_out->data, gp.vo_sb = v_out->stride_b, gp.vo_sh = v_out->stride_h, gp.vo_st = v_out->stride_t;
+  hipError_t e = launch_gather(gp, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "gather kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

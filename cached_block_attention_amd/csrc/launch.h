@@ -1,0 +1,102 @@
+// Internal launch descriptors shared by the host API and the HIP kernels of
+// libblkattn.so. Not part of the public ABI (include/blkattn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blkattn {
+
+// Keys per staged tile of the bf16 MFMA kernel and of the split plan.
+constexpr int kTileKeys = 64;
+
+// The concatenated key sequence one (batch, kv-head) attends:
+// [prefix rows (optionally gathered through idx); block rows].
+struct KeySeq {
+  const void* k_pre;
+  const void* v_pre;
+  int64_t kp_sb, kp_sh, kp_st;  // element strides of k_pre
+  int64_t vp_sb, vp_sh, vp_st;  // element strides of v_pre
+  const int32_t* idx;           // [B, Hkv, n_pre] or nullptr
+  int64_t p_rows;               // rows of k_pre/v_pre (clamp bound for idx)
+  int64_t n_pre;                // prefix keys attended (P, or n_keep with idx)
+  const void* k_blk;
+  const void* v_blk;
+  int64_t kb_sb, kb_sh, kb_st;
+  int64_t vb_sb, vb_sh, vb_st;
+  int32_t n_blk;                // block keys attended (Bq, or 0)
+};
+
+// Where a partial-attention launch writes.
+enum OutMode : int32_t {
+  kOutFinal = 0,    // O in the input dtype (strided) + optional LSE
+  kOutPartial = 1,  // contiguous fp32 partial (o, m, l); split s at offset s*split rows
+};
+
+struct OutDesc {
+  int32_t mode;
+  void* o;                      // final O
+  int64_t o_sb, o_sh, o_st;
+  float* lse;                   // final LSE or nullptr
+  float* po;                    // partial o base
+  float* pm;                    // partial m base
+  float* pl;                    // partial l base
+  int64_t split_rows;           // rows of one split's partial (B*Hq*Bq) when split
+};
+
+struct AttnParams {
+  int32_t batch, q_heads, kv_heads, group, head_dim, block_len;
+  const void* q;
+  int64_t q_sb, q_sh, q_st;
+  KeySeq keys;
+  OutDesc out;
+  float scale;          // score scale (natural-log units)
+  float scale_log2;     // scale * log2(e): scores in base-2 units
+  int32_t splits;       // key splits (gridDim.x)
+  int32_t tiles;        // ceil((n_pre + n_blk) / tile keys of this kernel)
+  int32_t rows_per_wg;  // packed (q-head, query) rows one workgroup owns
+  int32_t row_chunks;   // workgroups along the packed rows of one kv-head
+};
+
+// Inputs of an N-way log-sum-exp merge of partials (same rows, disjoint keys).
+struct MergeParams {
+  int32_t batch, q_heads, block_len, head_dim;
+  int32_t nsrc;               // number of partials merged
+  const float* src_o[2];      // explicit sources (nsrc == 2 and strided == 0)
+  const float* src_m[2];
+  const float* src_l[2];
+  int32_t strided;            // 1: sources are src_*[0] + s * split_rows
+  int64_t split_rows;
+  int32_t out_dtype;          // BLKATTN_F32 / BLKATTN_BF16 for o_final
+  void* o_final;              // strided O or nullptr
+  int64_t o_sb, o_sh, o_st;
+  float* lse;                 // or nullptr
+  float* out_o;               // merged partial or nullptr
+  float* out_m;
+  float* out_l;
+};
+
+struct GatherParams {
+  int32_t batch, kv_heads, head_dim, elt_bytes;
+  int64_t p_rows, n_keep;
+  const int32_t* idx;
+  const void* k_full;
+  const void* v_full;
+  int64_t kf_sb, kf_sh, kf_st, vf_sb, vf_sh, vf_st;
+  void* k_out;
+  void* v_out;
+  int64_t ko_sb, ko_sh, ko_st, vo_sb, vo_sh, vo_st;
+};
+
+// Kernel launchers (return the hipError_t of the launch).
+hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,
+                             hipStream_t stream);
+
+// Tile keys the bf16 kernel stages per step for a given wave count.
+int bf16_tile_keys(int waves);
+
+}  // namespace blkattn

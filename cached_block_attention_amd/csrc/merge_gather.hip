@@ -1,0 +1,158 @@
+// Log-sum-exp merge of partial attention states, the retained-row gather, and
+// the empty-state fill, for gfx950. All three are HBM-bound streaming kernels.
+//
+// Merge: for partials (o_s, m_s, l_s) of the same query rows over disjoint key
+// sets, M = max_s m_s, w_s = l_s e^{m_s - M}, l = sum_s w_s,
+// o = sum_s w_s o_s / l, LSE = M + ln l. Continuing the online-softmax
+// recurrence (eqs. 2-6 of section 3.3.3 of "LaCache: Exact Caching and
+// Precision-Adaptive Inference for Diffusion Large Language Models") from a
+// cached state over further key tiles gives exactly this; the same kernel
+// reduces the key splits of one attention call (fixed order over s, so the
+// result is bitwise reproducible).
+//
+// Gather: k_out[b, h, r] = k_full[b, h, idx[b, h, r]] (and v), a bit copy of the
+// retained rows (aitopics "kv state" page, Sparse-dLLM abstract).
+#include "launch.h"
+
+#include <math.h>
+
+namespace blkattn {
+namespace {
+
+// One thread merges 4 consecutive head-dim values of one row; D/4 threads of
+// the same wave share a row, so a row's m and l are read by all of its lanes in
+// the same instruction, before any lane writes them (safe in-place update).
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t rows = (int64_t)p.batch * p.q_heads * p.block_len;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+
+  auto src_o = [&](int s) -> const float* {
+    return p.strided ? p.src_o[0] + ((int64_t)s * p.split_rows + row) * D : p.src_o[s] + row * D;
+  };
+  auto src_m = [&](int s) -> float {
+    return p.strided ? p.src_m[0][(int64_t)s * p.split_rows + row] : p.src_m[s][row];
+  };
+  auto src_l = [&](int s) -> float {
+    return p.strided ? p.src_l[0][(int64_t)s * p.split_rows + row] : p.src_l[s][row];
+  };
+
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsrc; ++s) M = fmaxf(M, src_m(s));
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.nsrc; ++s) {
+      const float ms = src_m(s);
+      const float w = (ms == -INFINITY) ? 0.0f : src_l(s) * expf(ms - M);
+      const float4 os = *(const float4*)(src_o(s) + 4 * c4);
+      L += w;
+      acc.x = fmaf(w, os.x, acc.x);
+      acc.y = fmaf(w, os.y, acc.y);
+      acc.z = fmaf(w, os.z, acc.z);
+      acc.w = fmaf(w, os.w, acc.w);
+    }
+  }
+  const bool live = L > 0.0f;
+  const float inv = live ? 1.0f / L : 0.0f;
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const float mo = live ? M : -INFINITY;
+
+  if (p.o_final != nullptr) {
+    const int64_t hb = row / p.block_len;       // b * Hq + hq
+    const int64_t qi = row - hb * p.block_len;
+    const int64_t b = hb / p.q_heads, hq = hb - (hb / p.q_heads) * p.q_heads;
+    const int64_t off = b * p.o_sb + hq * p.o_sh + qi * p.o_st + 4 * c4;
+    if (p.out_dtype == 0) {
+      *(float4*)((float*)p.o_final + off) = o;
+    } else {
+      const __bf16 v0 = (__bf16)o.x, v1 = (__bf16)o.y, v2 = (__bf16)o.z, v3 = (__bf16)o.w;
+      uint2 w;
+      w.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+      w.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+      *(uint2*)((uint16_t*)p.o_final + off) = w;
+    }
+  }
+  if (p.lse != nullptr && c4 == 0) p.lse[row] = live ? M + logf(L) : -INFINITY;
+  if (p.out_o != nullptr) {
+    *(float4*)(p.out_o + row * D + 4 * c4) = o;
+    if (c4 == 0) {
+      p.out_m[row] = mo;
+      p.out_l[row] = live ? L : 0.0f;
+    }
+  }
+}
+
+// One thread copies one 16-byte chunk of one retained row of K and of V.
+__global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
+  const int cpr = p.head_dim * p.elt_bytes / 16;
+  const int64_t total = (int64_t)p.batch * p.kv_heads * p.n_keep * cpr;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t rowi = e / cpr;
+  const int c = (int)(e - rowi * cpr);
+  const int64_t bh = rowi / p.n_keep;
+  const int64_t r = rowi - bh * p.n_keep;
+  const int64_t b = bh / p.kv_heads, h = bh - (bh / p.kv_heads) * p.kv_heads;
+  int64_t src = p.idx[rowi];
+  src = src < 0 ? 0 : (src >= p.p_rows ? p.p_rows - 1 : src);
+  const int64_t eb = p.elt_bytes;
+  const char* ks = (const char*)p.k_full + (b * p.kf_sb + h * p.kf_sh + src * p.kf_st) * eb;
+  const char* vs = (const char*)p.v_full + (b * p.vf_sb + h * p.vf_sh + src * p.vf_st) * eb;
+  char* kd = (char*)p.k_out + (b * p.ko_sb + h * p.ko_sh + r * p.ko_st) * eb;
+  char* vd = (char*)p.v_out + (b * p.vo_sb + h * p.vo_sh + r * p.vo_st) * eb;
+  const uint4 kv = *(const uint4*)(ks + 16 * c);
+  const uint4 vv = *(const uint4*)(vs + 16 * c);
+  *(uint4*)(kd + 16 * c) = kv;
+  *(uint4*)(vd + 16 * c) = vv;
+}
+
+// Empty key set: o = 0, m = -inf, l = 0.
+__global__ __launch_bounds__(256) void fill_empty_kernel(float* o, float* m, float* l, int64_t rows,
+                                                         int head_dim) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < rows * head_dim) o[e] = 0.0f;
+  if (e < rows) {
+    m[e] = -INFINITY;
+    l[e] = 0.0f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.batch * p.q_heads * p.block_len;
+  if (rows == 0) return hipSuccess;
+  if (p.head_dim == 128) {
+    const int64_t blocks = (rows + 7) / 8;
+    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else if (p.head_dim == 64) {
+    const int64_t blocks = (rows + 15) / 16;
+    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
+  const int64_t total = (int64_t)p.batch * p.kv_heads * p.n_keep * (p.head_dim * p.elt_bytes / 16);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,
+                             hipStream_t stream) {
+  const int64_t total = rows * head_dim;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     o, m, l, rows, head_dim);
+  return hipGetLastError();
+}
+
+}  // namespace blkattn

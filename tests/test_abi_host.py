@@ -1,0 +1,107 @@
+"""Host-side checks of libblkattn.so: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import cached_block_attention_amd as ba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    txt = open(os.path.join(ROOT, "include", "blkattn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(blkattn_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ba.LIB_PATH):
+        pytest.skip("libblkattn.so not built")
+    return ba.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) == 11, syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_and_strings(lib):
+    assert lib.blkattn_abi_version() == 1
+    assert lib.blkattn_strerror(ba.ERR_WORKSPACE) == b"workspace missing or too small"
+    assert lib.blkattn_strerror(12345) == b"unknown status"
+
+
+def dims(**kw):
+    base = dict(batch=4, q_heads=28, kv_heads=4, head_dim=128, block_len=32, n_keep=0,
+                prefix_len=32768, dtype=ba.BF16, scale=0.08838834764831845, splits=0, reserved=0)
+    base.update(kw)
+    return ba.Dims(**base)
+
+
+def call_full(lib, d, **ptrs):
+    t = ba.Tensor(ptrs.get("data", 4096), 128 * 32, 128 * 32, 128)
+    tp = ba.Tensor(ptrs.get("data", 4096), 128 * 32768, 128 * 32768, 128)
+    return lib.blkattn_full(ctypes.byref(d), ctypes.byref(t), ctypes.byref(tp), ctypes.byref(tp),
+                            ptrs.get("idx"), ctypes.byref(t), ctypes.byref(t), ctypes.byref(t),
+                            None, ptrs.get("ws"), ptrs.get("ws_bytes", 0), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_heads=28, kv_heads=5), ba.ERR_INVALID_ARG),
+    (dict(kv_heads=0), ba.ERR_INVALID_ARG),
+    (dict(batch=-1), ba.ERR_INVALID_ARG),
+    (dict(head_dim=96), ba.ERR_UNSUPPORTED),
+    (dict(dtype=7), ba.ERR_UNSUPPORTED),
+    (dict(scale=0.0), ba.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ba.ERR_INVALID_ARG),
+    (dict(reserved=1), ba.ERR_INVALID_ARG),
+    (dict(n_keep=5), ba.ERR_INVALID_ARG),      # n_keep set without indices
+])
+def test_bad_dims_rejected(lib, kw, status):
+    assert call_full(lib, dims(**kw)) == status
+    assert lib.blkattn_last_error() != b""
+
+
+def test_workspace_and_alignment_rejected(lib):
+    d = dims()
+    need = lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL)
+    assert need > 0
+    assert call_full(lib, d) == ba.ERR_WORKSPACE                        # none given
+    assert call_full(lib, d, ws=4096, ws_bytes=need - 1) == ba.ERR_WORKSPACE
+    assert call_full(lib, d, data=4100, ws=4096, ws_bytes=need) == ba.ERR_MISALIGNED
+
+
+def test_degenerate_sizes_are_noops(lib):
+    for kw in (dict(batch=0), dict(q_heads=0), dict(block_len=0)):
+        d = dims(**kw)
+        assert lib.blkattn_full(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                                None, 0, None) == ba.OK
+
+
+def test_split_plan_is_a_function_of_dims(lib):
+    # the metric workload: 16 (batch, kv-head) groups -> 32 key splits of ~16 tiles
+    d = dims()
+    assert lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_FULL) == 32
+    rows = 4 * 28 * 32
+    assert lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL) >= 32 * rows * (128 + 2) * 4
+    d1 = dims(splits=1)
+    assert lib.blkattn_plan_splits(ctypes.byref(d1), ba.OP_FULL) == 1
+    assert lib.blkattn_workspace_bytes(ctypes.byref(d1), ba.OP_FULL) == 0
+    tiny = dims(batch=1, q_heads=4, kv_heads=4, head_dim=64, prefix_len=256, dtype=ba.F32)
+    assert lib.blkattn_plan_splits(ctypes.byref(tiny), ba.OP_FULL) == 1
+    huge = dims(splits=100000)
+    assert lib.blkattn_plan_splits(ctypes.byref(huge), ba.OP_FULL) == (32768 + 32 + 63) // 64
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 32, 64)
+    with pytest.raises(ValueError):
+        ba.attention(q, q, q, q, q)

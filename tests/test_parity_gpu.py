@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (max abs error vs the oracle): fp32 workloads 1e-5 on O and LSE;
+bf16 workloads 1.5e-2 on O (and partial o) and 1e-3 on LSE (partials: m + ln l);
+the gather is compared bit for bit. Small cases span several 64-key tiles,
+ragged key and query tails, every wave count of the GQA packing and forced
+split counts; the full-size workloads run in the launch configuration the
+benchmark times and are checked on sampled (batch, q-head) pairs.
+"""
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from tests.gpu_util import TOL, bits, down, lse_of, max_err, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ba():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cached_block_attention_amd as mod
+    mod.library()   # fails loudly when the library is missing
+    return mod
+
+
+def shape(name="dream_gqa", **kw):
+    return datagen.scaled_shape(name, **kw)
+
+
+def upload(inp):
+    d = {k: up(getattr(inp, k)) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
+    d["idx"] = up(inp.idx) if inp.idx is not None else None
+    return d
+
+
+def check_full(ba, sh, splits=0, heads=None, seed_base=None):
+    say(f"case full {sh} splits={splits}")
+    inp = datagen.make_inputs(sh, seed_base)
+    t = upload(inp)
+    o, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"],
+                          splits=splits)
+    import torch
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale,
+                                 idx=inp.idx, heads=heads)
+    mask = ~np.isnan(lse_ref)
+    tol = TOL[sh.dtype]
+    eo = max_err(down(o), o_ref, mask[..., None].repeat(o_ref.shape[-1], -1))
+    el = max_err(down(lse), lse_ref, mask)
+    say(f"  max err O {eo:.3e} LSE {el:.3e}")
+    assert eo <= tol["o"] and el <= tol["lse"], (eo, el)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# blkattn_full on small shapes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_full_tiny_f32(ba, splits):
+    check_full(ba, datagen.WORKLOADS["tiny_f32"], splits=splits)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=2, q_heads=8, kv_heads=2, prefix_len=1000, block_len=32),    # G=4, ragged P
+    dict(batch=1, q_heads=4, kv_heads=4, prefix_len=777, block_len=32),     # G=1: one wave
+    dict(batch=1, q_heads=14, kv_heads=2, prefix_len=500, block_len=64),    # 448 rows: 2 chunks
+    dict(batch=2, q_heads=6, kv_heads=2, prefix_len=300, block_len=20),     # ragged rows
+    dict(batch=1, q_heads=4, kv_heads=2, prefix_len=200, block_len=32, head_dim=64),
+    dict(batch=1, q_heads=2, kv_heads=1, prefix_len=0, block_len=32),       # block only
+    dict(batch=1, q_heads=1, kv_heads=1, prefix_len=70, block_len=1),       # one query
+    dict(batch=1, q_heads=40, kv_heads=5, prefix_len=130, block_len=32),    # 8 waves
+    dict(batch=1, q_heads=3, kv_heads=1, prefix_len=64, block_len=32),      # 3 waves, exact tiles
+], ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+@pytest.mark.parametrize("splits", [0, 1, 2, 5])
+def test_full_bf16_shapes(ba, kw, splits):
+    check_full(ba, shape(**kw), splits=splits)
+
+
+def test_full_f32_head_dim_128(ba):
+    check_full(ba, datagen.scaled_shape("tiny_f32", head_dim=128, q_heads=4, kv_heads=2,
+                                        prefix_len=100, block_len=40), splits=2)
+
+
+def test_full_with_outliers(ba):
+    sh = shape(batch=2, prefix_len=2048)
+    assert sh.outlier_frac > 0
+    check_full(ba, sh)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 4])
+def test_full_gathered_prefix(ba, splits):
+    check_full(ba, datagen.scaled_shape("sparse_gqa", prefix_len=3000, n_keep=700), splits=splits)
+
+
+def test_zero_queries_give_column_mean(ba):
+    import torch
+    sh = shape(batch=1, q_heads=4, kv_heads=2, prefix_len=300, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    q = torch.zeros_like(t["q"])
+    o, lse = ba.attention(q, t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+    for h in range(4):
+        vals = np.concatenate([oracle.widen(inp.v_pre[0, h // 2]), oracle.widen(inp.v_blk[0, h // 2])])
+        assert max_err(down(o)[0, h], np.broadcast_to(vals.mean(0), (32, 128))) <= TOL["bf16"]["o"]
+    assert max_err(down(lse), np.log(332.0)) <= TOL["bf16"]["lse"]
+
+
+def test_gqa_equals_repeated_mha(ba):
+    import torch
+    sh = shape(batch=1, q_heads=6, kv_heads=2, prefix_len=400, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    o1, l1 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], splits=2)
+    rep = lambda x: x.repeat_interleave(3, dim=1).contiguous()  # noqa: E731
+    o2, l2 = ba.attention(t["q"], rep(t["k_pre"]), rep(t["v_pre"]), rep(t["k_blk"]), rep(t["v_blk"]),
+                          splits=2)
+    torch.cuda.synchronize()
+    assert max_err(down(o1), down(o2)) <= 1e-2 and max_err(down(l1), down(l2)) <= 1e-4
+
+
+def test_strided_views(ba):
+    # q and k/v given as non-contiguous views (head-major storage transposed)
+    import torch
+    sh = shape(batch=2, q_heads=4, kv_heads=2, prefix_len=333, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    tv = {k: t[k].transpose(1, 2).contiguous().transpose(1, 2) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
+    assert not tv["k_pre"].is_contiguous()
+    o = torch.empty(2, 32, 4, 128, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    lse = torch.empty(2, 4, 32, dtype=torch.float32, device="cuda")
+    ba.blkattn_full(tv["q"], tv["k_pre"], tv["v_pre"], tv["k_blk"], tv["v_blk"], o, lse)
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale)
+    assert max_err(down(o), o_ref) <= TOL["bf16"]["o"] and max_err(down(lse), lse_ref) <= TOL["bf16"]["lse"]
+
+
+def test_deterministic_bits(ba):
+    import torch
+    sh = shape(batch=2, prefix_len=3000)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    o1, l1 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+    o2, l2 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))
+
+
+# ---------------------------------------------------------------------------
+# partials, merge (the cached-prefix path) and gather
+# ---------------------------------------------------------------------------
+
+def _partial_ref(inp, sh, prefix=True):
+    if prefix:
+        return oracle.partial(inp.q, inp.k_pre, inp.v_pre, sh.scale, idx=inp.idx)
+    return oracle.partial(inp.q, inp.k_blk, inp.v_blk, sh.scale)
+
+
+def _check_partial(got, ref, dtype):
+    o, m, l = (down(x) for x in got)
+    ro, rm, rl = ref
+    eo = max_err(o, ro)
+    el = max_err(lse_of(m, l), lse_of(rm, rl))
+    say(f"  partial err o {eo:.3e} lse {el:.3e}")
+    assert eo <= TOL[dtype]["o"] and el <= TOL[dtype]["lse"], (eo, el)
+    assert np.all(l[np.isfinite(m)] >= 1.0 - 1e-4)        # the max term contributes 1
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {}),
+    ("dream_gqa", dict(batch=2, prefix_len=1500)),
+    ("llada_bf16", dict(q_heads=4, kv_heads=4, prefix_len=900)),
+    ("sparse_gqa", dict(prefix_len=2000, n_keep=333)),
+])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_prefix_block_partials_and_merge(ba, name, kw, splits):
+    import torch
+    sh = datagen.scaled_shape(name, **kw)
+    say(f"case partials {sh} splits={splits}")
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"], idx=t["idx"], splits=splits)
+    pb = ba.block_partial(t["q"], t["k_blk"], t["v_blk"])
+    o, lse = ba.merge(pp, pb, dtype=t["q"].dtype)
+    torch.cuda.synchronize()
+    _check_partial(pp, _partial_ref(inp, sh, True), sh.dtype)
+    _check_partial(pb, _partial_ref(inp, sh, False), sh.dtype)
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=inp.idx)
+    assert max_err(down(o), o_ref) <= TOL[sh.dtype]["o"]
+    assert max_err(down(lse), lse_ref) <= TOL[sh.dtype]["lse"]
+    # in-place update of the cached state: ab aliases a
+    ba.blkattn_merge(pp, pb, ab=pp)
+    torch.cuda.synchronize()
+    ro, rm, rl, rlse = oracle.merge(_partial_ref(inp, sh, True), _partial_ref(inp, sh, False))
+    assert max_err(down(pp.o), ro) <= TOL[sh.dtype]["o"]
+    assert max_err(lse_of(down(pp.m), down(pp.l)), rlse) <= TOL[sh.dtype]["lse"]
+
+
+def test_empty_prefix_partial_and_merges(ba):
+    import torch
+    sh = shape(batch=1, q_heads=4, kv_heads=2, prefix_len=0, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    pe = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"])
+    torch.cuda.synchronize()
+    assert np.all(down(pe.o) == 0) and np.all(np.isneginf(down(pe.m))) and np.all(down(pe.l) == 0)
+    pb = ba.block_partial(t["q"], t["k_blk"], t["v_blk"])
+    o, lse = ba.merge(pe, pb, dtype=torch.float32)
+    o2, lse2 = ba.merge(pb, pe, dtype=torch.float32)
+    torch.cuda.synchronize()
+    # w*o/w in fp32: equal to the block partial up to rounding
+    assert max_err(down(o), down(pb.o)) <= 1e-6 and max_err(down(o2), down(pb.o)) <= 1e-6
+    assert max_err(down(lse), lse_of(down(pb.m), down(pb.l))) <= 1e-6
+    oe, le = ba.merge(pe, pe, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.all(down(oe) == 0) and np.all(np.isneginf(down(le)))
+
+
+@pytest.mark.parametrize("dtype_name,kw", [("bf16", dict(prefix_len=3000, n_keep=700)),
+                                           ("f32", dict(prefix_len=500, n_keep=77))])
+def test_gather_bit_exact(ba, dtype_name, kw):
+    base = "sparse_gqa" if dtype_name == "bf16" else "tiny_f32"
+    sh = datagen.scaled_shape(base, **kw)
+    if dtype_name == "f32":
+        import dataclasses
+        sh = dataclasses.replace(sh, n_keep=kw["n_keep"])
+    inp = datagen.make_inputs(sh)
+    if inp.idx is None:
+        inp.idx = datagen.retained_indices(sh.batch, sh.kv_heads, sh.prefix_len, kw["n_keep"], 77)
+    t = upload(inp)
+    idx = up(inp.idx)
+    ko, vo = ba.gather_prefix(t["k_pre"], t["v_pre"], idx)
+    assert np.array_equal(bits(ko), oracle.gather(inp.k_pre, inp.idx))
+    assert np.array_equal(bits(vo), oracle.gather(inp.v_pre, inp.idx))
+
+
+def test_gather_then_dense_matches_fused(ba):
+    import torch
+    sh = datagen.scaled_shape("sparse_gqa", prefix_len=5000, n_keep=1000)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    ko, vo = ba.gather_prefix(t["k_pre"], t["v_pre"], t["idx"])
+    o1, l1 = ba.attention(t["q"], ko, vo, t["k_blk"], t["v_blk"], splits=4)
+    o2, l2 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"], splits=4)
+    torch.cuda.synchronize()
+    # same keys in the same tile order: identical bits
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))
+
+
+def test_identity_indices_equal_dense(ba):
+    import torch
+    sh = shape(batch=1, q_heads=7, kv_heads=1, prefix_len=600, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    ident = torch.arange(600, dtype=torch.int32, device="cuda").view(1, 1, 600).contiguous()
+    o1, l1 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=ident, splits=3)
+    o2, l2 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], splits=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2)) and np.array_equal(bits(l1), bits(l2))

@@ -23,10 +23,10 @@ thread_local char g_err[512] = "";
 thread_local void* g_ev_start = nullptr;
 thread_local void* g_ev_stop = nullptr;
 
-// Workgroups the automatic plan aims for: two per compute unit of a 256-CU
-// MI355X. A fixed target keeps the plan (and so the bits of the result) a
-// function of the dims alone.
-constexpr int64_t kTargetWorkgroups = 512;
+// The automatic plan aims for as many workgroups as the 256 compute units of
+// an MI355X hold at once. A fixed target keeps the plan (and so the bits of the
+// result) a function of the dims alone.
+constexpr int64_t kComputeUnits = 256;
 // Each key split keeps at least this many 64-key tiles, which bounds the
 // split-partial traffic (d+2 fp32 per row per split) relative to the K/V
 // stream.
@@ -99,25 +99,23 @@ struct Plan {
   int splits = 1;
 };
 
-Plan make_plan(const blkattn_dims* d, int64_t n_keys) {
+Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
   Plan pl;
   const int64_t G = d->q_heads / d->kv_heads;
   const int64_t R = G * d->block_len;
-  int64_t base;
+  int64_t base, per_cu = 1;
   if (d->dtype == BLKATTN_F32) {
     pl.tile_keys = 32;
     base = (int64_t)d->batch * d->q_heads;
+    per_cu = 8;
   } else {
-    if (R <= 32) {
-      pl.waves = 1;
-      pl.row_chunks = 1;
-    } else {
-      pl.row_chunks = (int)((R + 255) / 256);
-      pl.waves = (int)((R + 32 * pl.row_chunks - 1) / (32 * pl.row_chunks));
-    }
+    pl.row_chunks = R > 256 ? (int)((R + 255) / 256) : 1;
+    const int64_t rows = (R + pl.row_chunks - 1) / pl.row_chunks;
+    pl.waves = bf16_waves_for_rows(rows);
     pl.rows_per_wg = 32 * pl.waves;
     pl.tile_keys = bf16_tile_keys(pl.waves);
     base = (int64_t)d->batch * d->kv_heads * pl.row_chunks;
+    per_cu = bf16_workgroups_per_cu(pl.waves);
   }
   pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
   const int64_t tiles64 = (n_keys + 63) / 64;
@@ -125,13 +123,20 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys) {
   if (d->splits > 0) {
     s = d->splits;
   } else {
-    s = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
+    const int64_t target = kComputeUnits * per_cu;
+    s = base > 0 ? (target + base - 1) / base : 1;
     const int64_t cap = tiles64 / kMinTilesPerSplit;
     if (s > cap) s = cap;
   }
   if (s > tiles64) s = tiles64;
   if (s > pl.tiles) s = pl.tiles;
   if (s < 1) s = 1;
+  if (indexed && d->dtype == BLKATTN_BF16) {
+    // every split stages its retained-row indices in LDS
+    const int64_t per = bf16_index_cap() / pl.tile_keys;  // tiles per split at most
+    const int64_t need = (pl.tiles + per - 1) / per;
+    if (s < need) s = need;
+  }
   pl.splits = (int)s;
   return pl;
 }
@@ -247,9 +252,10 @@ int blkattn_plan_splits(const blkattn_dims* d, int op) {
   if (st != BLKATTN_OK) return st;
   if (op != BLKATTN_OP_FULL && op != BLKATTN_OP_PREFIX_PARTIAL)
     return fail(BLKATTN_ERR_INVALID_ARG, "unknown op %d", op);
-  const int64_t n_pre = d->n_keep > 0 ? d->n_keep : d->prefix_len;
+  const bool indexed = d->n_keep > 0;
+  const int64_t n_pre = indexed ? d->n_keep : d->prefix_len;
   const int64_t n_keys = n_pre + (op == BLKATTN_OP_FULL ? d->block_len : 0);
-  return make_plan(d, n_keys).splits;
+  return make_plan(d, n_keys, indexed).splits;
 }
 
 size_t blkattn_workspace_bytes(const blkattn_dims* d, int op) {
@@ -277,7 +283,7 @@ int blkattn_full(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_t
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
   const int64_t n_keys = n_pre + d->block_len;
-  const Plan pl = make_plan(d, n_keys);
+  const Plan pl = make_plan(d, n_keys, idx != nullptr);
   const WsLayout wl = ws_layout(d, pl.splits);
   if (wl.total > 0) {
     if (workspace == nullptr || workspace_bytes < wl.total)
@@ -340,7 +346,7 @@ int blkattn_prefix_partial(const blkattn_dims* d, const blkattn_tensor* q, const
     if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "fill kernel launch failed: %s", hipGetErrorString(e));
     return ok();
   }
-  const Plan pl = make_plan(d, n_pre);
+  const Plan pl = make_plan(d, n_pre, idx != nullptr);
   const WsLayout wl = ws_layout(d, pl.splits);
   if (wl.total > 0) {
     if (workspace == nullptr || workspace_bytes < wl.total)
@@ -390,7 +396,7 @@ int blkattn_block_partial(const blkattn_dims* d, const blkattn_tensor* q, const 
   if ((st = check_partial(out, "out", rows))) return st;
   blkattn_dims d1 = *d;
   d1.splits = 1;  // no workspace on this path: one split over the block's keys
-  const Plan pl = make_plan(&d1, d->block_len);
+  const Plan pl = make_plan(&d1, d->block_len, false);
   AttnParams p = attn_params(&d1, q, pl);
   fill_keys(p.keys, &d1, nullptr, nullptr, nullptr, k_blk, v_blk, 0, d->block_len);
   p.out.mode = kOutPartial;

@@ -7,30 +7,37 @@
 // through retained-row indices); block], streamed tile by tile with the
 // recurrence of eqs. 2-6 in section 3.3.3 of "LaCache: Exact Caching and
 // Precision-Adaptive Inference for Diffusion Large Language Models" (running
-// max m, rescale alpha = exp(m_old - m_new), P~ = exp(S - m), l and O~
-// updates), finished as o = O~ / l (same page, Appendix J pseudocode). There is
-// no mask: the block is bidirectional.
+// max, rescale by exp(m_old - m_new), P~ = exp(S - m), l and O~ updates),
+// finished as o = O~ / l (same page, Appendix J pseudocode). There is no mask:
+// the block is bidirectional.
 //
 // How it maps to the hardware:
 //  * One workgroup per (key split, kv-head, packed-row chunk, batch). The rows
 //    of all G q-heads of a kv-head are packed (row = g * Bq + i), so every K/V
 //    tile staged in LDS feeds all of them: K/V is read from HBM once per
 //    kv-head and split (GQA packing).
+//  * K/V tiles stream HBM -> LDS with direct-to-LDS DMA loads
+//    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no
+//    register staging) into a ring of NS stages, so NS-1 tiles are in flight
+//    while one is computed; one barrier per tile. Rows are stored with an XOR
+//    swizzle of their 16-byte chunks, chosen on the global side of the DMA.
 //  * Each wave owns 32 packed rows. Scores are computed transposed,
-//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: keys on the M side (LDS
-//    operand), queries on the N side (Q stays in registers for the whole key
-//    loop). A lane then holds one query row's scores for 16 keys per 32-key
-//    block, so the row max and row sum are lane-local plus one exchange
-//    between the two wave halves (v_permlane32_swap).
-//  * The output is accumulated transposed too, O^T += V^T P^T: P^T comes
-//    straight from the score registers (converted to bf16), V^T is read from
-//    LDS, where V is stored key-contiguous per head-dim row with the keys
-//    permuted so that each lane's 8 keys are one 16-byte read.
-//  * K/V tiles move HBM -> registers (16-byte loads, one tile ahead) ->
-//    LDS (two buffers, rows padded against bank conflicts), one barrier per
-//    tile.
-//  * Softmax runs in base 2: scores are scaled by scale*log2(e) inside one FMA
-//    before v_exp_f32; m is exported in natural-log units.
+//    S^T = K Q^T (v_mfma_f32_32x32x16_bf16; keys on the M side read from LDS,
+//    queries on the N side held in registers for the whole loop), so a lane
+//    holds one query row's scores for 16 keys per 32-key block: the row max
+//    and sum are lane-local plus one exchange between the wave halves.
+//  * The output is accumulated transposed, O^T += V^T P^T: P^T comes straight
+//    from the score registers (converted to bf16), and V^T is read from the
+//    row-major V tile with ds_read_b64_tr_b16 (transposing LDS reads).
+//  * Softmax runs in base 2 (scale * log2(e) folded into one FMA before
+//    v_exp_f32). The reference max is only moved when a tile's max exceeds it
+//    by more than kSlack (2^8): the O~ rescale is skipped otherwise, which is
+//    exact because l and O~ always share the same reference. The true running
+//    max is tracked separately and exported in natural-log units.
+//  * The weights enter the PV product rounded to bf16. O~ is normalised by the
+//    sum of those rounded weights (v_dot2_f32_bf16 against (1, 1)), so o is an
+//    exact convex combination of V rows with the weights actually used; l and
+//    the log-sum-exp use the sum of the unrounded weights.
 #include "launch.h"
 
 #include <math.h>
@@ -38,17 +45,28 @@
 namespace blkattn {
 namespace {
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kSlack = 8.0f;  // log2 of the largest unnormalised weight allowed
 
-// Position of tile key k inside a V^T row. Within each 16-key group the order
-// is keys 0-3, 8-11, 4-7, 12-15, which is the order in which the score
-// registers of the two wave halves hand keys to the PV product.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int o = k & 15;
-  return (k & ~15) | (((o >> 2) & 1) << 3) | ((o >> 3) << 2) | (o & 3);
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// XOR swizzle of the 16-byte chunk index of K row r (CPR chunks per row):
+// 16 consecutive rows read at one logical chunk land on distinct banks.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int r) {
+  return CPR == 16 ? (r & 15) : ((r ^ (r >> 3)) & 7);
+}
+
+// XOR swizzle of V row r for the transposing reads, where one read of 32 lanes
+// covers 4 rows x 64 bytes: it spreads the 4 rows over distinct chunk groups.
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r) {
+  return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
 __device__ __forceinline__ float pair_max(float x) {
@@ -61,87 +79,110 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Per-(batch, kv-head) view of the key sequence [prefix (gathered); block].
-struct SeqView {
-  const uint16_t* kpre;  // k_pre + b*sb + h*sh
-  const uint16_t* vpre;
-  const uint16_t* kblk;
-  const uint16_t* vblk;
-  const int32_t* idx;    // idx + (b*Hkv + h)*n_pre, or nullptr
-  int64_t kp_st, vp_st, kb_st, vb_st;
-  int64_t n_pre, p_rows;
-};
-
-// Element offset of key j's row and whether it lies in the prefix.
-__device__ __forceinline__ int64_t seq_row(const SeqView& sv, int64_t j, bool& pre) {
-  pre = j < sv.n_pre;
-  int64_t r = pre ? j : j - sv.n_pre;
-  if (sv.idx != nullptr && pre) {
-    const int64_t x = sv.idx[j];
-    r = x < 0 ? 0 : (x >= sv.p_rows ? sv.p_rows - 1 : x);
-  }
-  return r;
+// s_waitcnt vmcnt(n) leaving the other counters free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ const uint16_t* k_row(const SeqView& sv, int64_t j) {
-  bool pre;
-  const int64_t r = seq_row(sv, j, pre);
-  return pre ? sv.kpre + r * sv.kp_st : sv.kblk + r * sv.kb_st;
+// Wait until at most `ahead` later stages of this wave's DMAs are in flight.
+template <int IPW, int NS>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if (NS >= 4 && ahead >= 2) wait_vm<(NS >= 4 ? 2 : 0) * IPW>();
+  else if (NS >= 3 && ahead >= 1) wait_vm<(NS >= 3 ? 1 : 0) * IPW>();
+  else wait_vm<0>();
 }
 
-__device__ __forceinline__ const uint16_t* v_row(const SeqView& sv, int64_t j) {
-  bool pre;
-  const int64_t r = seq_row(sv, j, pre);
-  return pre ? sv.vpre + r * sv.vp_st : sv.vblk + r * sv.vb_st;
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would drain every outstanding DMA (vmcnt(0)) at each tile. LDS data is
+// ordered explicitly instead: DMA completion by s_waitcnt vmcnt before the
+// barrier, and every LDS read of a tile is consumed by an MFMA before the
+// barrier that lets its ring slot be refilled.
+__device__ __forceinline__ void tile_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
 }
 
-template <int D, int STAGE, int NW>
+// One direct-to-LDS DMA: 64 lanes x 16 bytes from per-lane global addresses
+// into 1 KB of LDS at lds_addr (wave-uniform, through M0). Written as inline
+// asm so that the compiler does not see an LDS write in flight and drain the
+// whole DMA ring (vmcnt(0)) before every LDS read; completion is ordered
+// explicitly by wait_stage() before the tile barrier. The instruction has no
+// register results.
+__device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+      : "memory", "m0");
+}
+
+constexpr int kIdxCap = 2048;  // retained-row indices staged per split
+
+template <int D, int NW, int TK, int NS>
 __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) {
-  constexpr int NT = 64 * NW;
-  constexpr int CPR = D / 8;               // 16-byte chunks per K row
-  constexpr int KCH = STAGE * CPR;         // K chunks per tile
-  constexpr int VUN = (STAGE / 2) * CPR;   // V units per tile (2 keys x 16 bytes)
-  constexpr int KIT = (KCH + NT - 1) / NT;
-  constexpr int VIT = (VUN + NT - 1) / NT;
-  // LDS rows are padded by 16 bytes: 16 consecutive rows read at the same
-  // column then fall on distinct banks, and every operand read of a lane is a
-  // fixed immediate offset from one base address.
-  constexpr int K_ROW = D * 2 + 16;        // bytes per K row
-  constexpr int VT_ROW = STAGE * 2 + 16;   // bytes per V^T row (one head-dim index)
-  constexpr int K_BYTES = STAGE * K_ROW;
-  constexpr int BUF_BYTES = K_BYTES + D * VT_ROW;
-  constexpr int NSB = STAGE / 32;          // 32-key score blocks per tile
+  constexpr int ROWB = D * 2;              // bytes per K/V row
+  constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  constexpr int KBYTES = TK * ROWB;        // K part of a stage
+  constexpr int STB = 2 * KBYTES;          // bytes per stage (K then V)
+  constexpr int INS = STB / 1024;          // DMA instructions per stage
+  constexpr int IPW = INS / NW;            // per wave
+  constexpr int RPI = 1024 / ROWB;         // rows per DMA instruction
+  constexpr int NSB = TK / 32;             // 32-key score blocks per tile
+  constexpr int NCC = TK / 16;             // 16-key chunks of the PV product
   constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O^T
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];
+  static_assert(INS % NW == 0, "every wave issues the same number of DMAs");
+  static_assert(IPW * (NS - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char ring[NS * STB];
+  __shared__ int32_t sidx[kIdxCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;    // wave half
-  const int n = lane & 31;    // query column of this lane / LDS row within a block
+  const int n = lane & 31;    // query column of this lane / operand row within a block
   const int split = blockIdx.x;
   const int hkv = blockIdx.y / p.row_chunks;
   const int rc = blockIdx.y - hkv * p.row_chunks;
   const int b = blockIdx.z;
   const int R = p.group * p.block_len;
-  const int64_t N = p.keys.n_pre + p.keys.n_blk;
   const int t0 = (int)((int64_t)split * p.tiles / p.splits);
   const int t1 = (int)((int64_t)(split + 1) * p.tiles / p.splits);
   const int nst = t1 - t0;
-  const int64_t kbeg = (int64_t)t0 * STAGE;
+  const int64_t kbeg = (int64_t)t0 * TK;
 
-  SeqView sv;
-  sv.kpre = (const uint16_t*)p.keys.k_pre + b * p.keys.kp_sb + hkv * p.keys.kp_sh;
-  sv.vpre = (const uint16_t*)p.keys.v_pre + b * p.keys.vp_sb + hkv * p.keys.vp_sh;
-  sv.kblk = (const uint16_t*)p.keys.k_blk + b * p.keys.kb_sb + hkv * p.keys.kb_sh;
-  sv.vblk = (const uint16_t*)p.keys.v_blk + b * p.keys.vb_sb + hkv * p.keys.vb_sh;
-  sv.idx = p.keys.idx ? p.keys.idx + ((int64_t)b * p.kv_heads + hkv) * p.keys.n_pre : nullptr;
-  sv.kp_st = p.keys.kp_st, sv.vp_st = p.keys.vp_st, sv.kb_st = p.keys.kb_st, sv.vb_st = p.keys.vb_st;
-  sv.n_pre = p.keys.n_pre, sv.p_rows = p.keys.p_rows;
+  // key sequence of this (batch, kv-head): byte pointers and row strides
+  const char* kpre = (const char*)p.keys.k_pre + 2 * (b * p.keys.kp_sb + hkv * p.keys.kp_sh);
+  const char* vpre = (const char*)p.keys.v_pre + 2 * (b * p.keys.vp_sb + hkv * p.keys.vp_sh);
+  const char* kblk = (const char*)p.keys.k_blk + 2 * (b * p.keys.kb_sb + hkv * p.keys.kb_sh);
+  const char* vblk = (const char*)p.keys.v_blk + 2 * (b * p.keys.vb_sb + hkv * p.keys.vb_sh);
+  const int64_t kp_st = 2 * p.keys.kp_st, vp_st = 2 * p.keys.vp_st;
+  const int64_t kb_st = 2 * p.keys.kb_st, vb_st = 2 * p.keys.vb_st;
+  const int64_t n_pre = p.keys.n_pre;
+  const int64_t n_all = p.keys.n_pre + p.keys.n_blk;
+  const bool indexed = p.keys.idx != nullptr;
+
+  // ---- retained-row indices of this split's prefix keys, staged in LDS ----
+  if (indexed) {
+    const int64_t lo = kbeg < n_pre ? kbeg : n_pre;
+    const int64_t hi0 = kbeg + (int64_t)nst * TK;
+    const int64_t hi = hi0 < n_pre ? hi0 : n_pre;
+    const int32_t* src = p.keys.idx + ((int64_t)b * p.kv_heads + hkv) * n_pre;
+    for (int64_t j = lo + tid; j < hi; j += 64 * NW) {
+      int64_t r = src[j];
+      r = r < 0 ? 0 : (r >= p.keys.p_rows ? p.keys.p_rows - 1 : r);
+      sidx[j - kbeg] = (int32_t)r;
+    }
+    __syncthreads();
+  }
 
   // ---- query fragment (B operand of S^T = K Q^T), resident for the loop ----
   const int prow = rc * p.rows_per_wg + wave * 32 + n;  // packed row of this lane
   const bool row_ok = prow < R;
+  const bool computes = rc * p.rows_per_wg + wave * 32 < R;  // wave-uniform
   int g = 0, qi = 0;
   if (row_ok) {
     g = prow / p.block_len;
@@ -159,95 +200,74 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
     }
   }
 
-  // ---- staging registers and the tile loader ----
-  // K: item e -> key e / CPR, 16-byte chunk e % CPR (consecutive lanes read one
-  // row contiguously). V: item u -> key pair u / CPR, chunk u % CPR; the pair is
-  // interleaved into 32-bit (key, key+1) words of V^T rows.
-  uint4 kreg[KIT];
-  uint4 vreg[VIT][2];
-
-  auto issue = [&](int st) {
-    const int64_t key0 = kbeg + (int64_t)st * STAGE;
-    const int64_t rem = N - key0;
-    const int nvalid = rem < STAGE ? (int)rem : STAGE;
+  // ---- DMA of one tile into a ring slot ----
+  // Instruction k of a stage fills 1 KB: K rows for k < INS/2, V rows after.
+  // Lane t writes LDS slot (row, physical chunk t % CPR), which holds the
+  // row's logical chunk (t % CPR) ^ swizzle(row).
+  const int lrow = lane / CPR;
+  const int lchunk = lane % CPR;
+  auto issue = [&](int t) {
+    char* slot = ring + (t % NS) * STB;
+    const int64_t key0 = kbeg + (int64_t)t * TK;
+    const bool dense = !indexed && key0 + TK <= n_pre;  // tile inside the dense prefix
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int e = tid + it * NT;
-      const int key = e / CPR, j = e % CPR;
-      kreg[it] = make_uint4(0, 0, 0, 0);
-      if ((KCH % NT == 0 || e < KCH) && key < nvalid)
-        kreg[it] = *(const uint4*)(k_row(sv, key0 + key) + 8 * j);
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int u = tid + it * NT;
-      const int k0 = 2 * (u / CPR), j = u % CPR;
-      vreg[it][0] = make_uint4(0, 0, 0, 0);
-      vreg[it][1] = make_uint4(0, 0, 0, 0);
-      if (VUN % NT == 0 || u < VUN) {
-        if (k0 < nvalid) vreg[it][0] = *(const uint4*)(v_row(sv, key0 + k0) + 8 * j);
-        if (k0 + 1 < nvalid) vreg[it][1] = *(const uint4*)(v_row(sv, key0 + k0 + 1) + 8 * j);
-      }
-    }
-  };
-
-  auto commit = [&](int buf) {
-    char* kb = smem + buf * BUF_BYTES;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int e = tid + it * NT;
-      if (KCH % NT == 0 || e < KCH) {
-        const int key = e / CPR, j = e % CPR;
-        *(uint4*)(kb + key * K_ROW + 16 * j) = kreg[it];
-      }
-    }
-    char* vt = kb + K_BYTES;
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int u = tid + it * NT;
-      if (VUN % NT == 0 || u < VUN) {
-        const int k0 = 2 * (u / CPR), j = u % CPR;
-        char* dst = vt + (8 * j) * VT_ROW + 2 * vt_pos(k0);
-        const uint32_t a[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
-        const uint32_t c[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const uint32_t w = (dd & 1) ? ((a[dd >> 1] >> 16) | (c[dd >> 1] & 0xffff0000u))
-                                      : ((a[dd >> 1] & 0xffffu) | (c[dd >> 1] << 16));
-          *(uint32_t*)(dst + dd * VT_ROW) = w;
+    for (int j = 0; j < IPW; ++j) {
+      const int k = wave * IPW + j;   // wave-uniform
+      const bool isv = k >= INS / 2;
+      const int kk = isv ? k - INS / 2 : k;
+      const int r = kk * RPI + lrow;
+      const int lc = lchunk ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+      const char* base = isv ? vpre : kpre;
+      int64_t st = isv ? vp_st : kp_st;
+      int64_t row = key0 + r;
+      if (!dense) {
+        int64_t key = row < n_all ? row : n_all - 1;  // rows past the end: any valid row (weight 0)
+        if (key < n_pre) {
+          row = indexed ? (int64_t)sidx[key - kbeg] : key;
+        } else {
+          row = key - n_pre;
+          base = isv ? vblk : kblk;
+          st = isv ? vb_st : kb_st;
         }
       }
+      dma_1k(base + row * st + 16 * lc,
+             (uint32_t)(uintptr_t)LDS_PTR(char, slot + k * 1024));
     }
   };
 
-  // ---- running state: O^T accumulators, base-2 running max, lane-partial sum ----
+  // ---- per-lane operand coordinates of the transposing V reads ----
+  // Source lane s = lane % 16 of each 16-lane group reads V row
+  // 16*cc + 8*rr + 4*h + s/4 at head-dim columns 32*db + 16*dh + 4*(s%4) .. +3;
+  // output lane (h, m) then holds V[16*cc + 8*rr + 4*h + e][32*db + m], e = 0..3.
+  const int vi = (lane & 15) >> 2;
+  const int vq = lane & 3;
+  const int vdh = (lane >> 4) & 1;
+
+  // ---- running state ----
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  float m2 = -INFINITY;
-  float lsum = 0.0f;
+  float m2 = -INFINITY;     // reference max (base 2) shared by l and O~
+  float mtrue = -INFINITY;  // exact running max (base 2)
+  float lsum = 0.0f;        // lane-partial sum of weights
+  float lhat = 0.0f;        // lane-partial sum of the bf16-rounded weights
   const float c2 = p.scale_log2;
-  // per-lane operand base offsets (the rest are immediates)
-  const int k_off = n * K_ROW + 16 * h;
-  const int v_off = n * VT_ROW + 16 * h;
 
-  if (nst > 0) {
-    issue(0);
-    commit(0);
-    if (nst > 1) issue(1);
-  }
-  __syncthreads();
+  wait_vm<0>();  // the query fragment has landed before any DMA is counted
+  const int npro = nst < NS - 1 ? nst : NS - 1;
+  for (int t = 0; t < npro; ++t) issue(t);
 
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) {
-      commit(buf ^ 1);
-      if (st + 2 < nst) issue(st + 2);
-    }
-    const char* kb = smem + buf * BUF_BYTES + k_off;
-    const char* vt = smem + buf * BUF_BYTES + K_BYTES + v_off;
+  for (int t = 0; t < nst; ++t) {
+    const int ahead = (nst - 1 - t) < (NS - 2) ? (nst - 1 - t) : (NS - 2);
+    wait_stage<IPW, NS>(ahead);
+    tile_barrier();
+    if (t + NS - 1 < nst) issue(t + NS - 1);
+    if (!computes) continue;
+
+    const char* kb = ring + (t % NS) * STB;
+    const char* vb = kb + KBYTES;
 
     // S^T blocks: keys 32*sb + (8*(r/4) + 4*h + r%4) x query n
     f32x16_t sacc[NSB];
@@ -255,17 +275,19 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
     for (int sb = 0; sb < NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.0f;
+      const int krow = 32 * sb + n;
+      const int ksw = swz_k<CPR>(krow);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *(const uint4*)(kb + (32 * sb) * K_ROW + 32 * kk);
+        const uint4 a = *(const uint4*)(kb + krow * ROWB + 16 * ((2 * kk + h) ^ ksw));
         sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[kk],
                                                            sacc[sb], 0, 0, 0);
       }
     }
 
     // keys past the end of the sequence (last tile only) get no weight
-    const int64_t rem = N - (kbeg + (int64_t)st * STAGE);
-    if (rem < STAGE) {
+    const int64_t rem = n_all - (kbeg + (int64_t)t * TK);
+    if (rem < TK) {
       const int nvalid = (int)rem;
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
@@ -276,51 +298,78 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
         }
     }
 
-    // online softmax (eqs. 2-5), base 2
+    // online softmax (eqs. 2-5) in base 2 with a lazily moved reference max
     float mx = sacc[0][0];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-    mx = pair_max(mx);
-    const float mnew = fmaxf(m2, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-    m2 = mnew;
+    const float mt = pair_max(mx) * c2;
+    mtrue = fmaxf(mtrue, mt);
+    if (__any(mt > m2 + kSlack)) {
+      const float mnew = fmaxf(m2, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
+      lhat *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
     float ps = 0.0f;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -mnew));
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -m2));
         sacc[sb][r] = e;
         ps += e;
       }
-    lsum = fmaf(lsum, alpha, ps);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    lsum += ps;
 
     // O^T += V^T P^T (eq. 6); chunk cc covers tile keys 16*cc .. 16*cc+15
 #pragma unroll
-    for (int cc = 0; cc < STAGE / 16; ++cc) {
+    for (int cc = 0; cc < NCC; ++cc) {
       bf16x8_t pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[cc >> 1][8 * (cc & 1) + i];
+      {
+        bf16x2_t one;
+        one[0] = (__bf16)1.0f;
+        one[1] = (__bf16)1.0f;
+        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, lhat, false);
+        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, lhat, false);
+        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, lhat, false);
+        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, lhat, false);
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint4 a = *(const uint4*)(vt + (32 * db) * VT_ROW + 32 * cc);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), pb,
-                                                           oacc[db], 0, 0, 0);
+        i16x4_t lo, hi;
+        {
+          const int row = 16 * cc + 4 * h + vi;
+          const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
+        }
+        {
+          const int row = 16 * cc + 8 + 4 * h + vi;
+          const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
+        }
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   // ---- finish: o = O~ / l, L = m + ln l (natural-log units) ----
   const float ltot = pair_sum(lsum);
+  const float lhtot = pair_sum(lhat);
   const bool live = ltot > 0.0f;
-  const float inv = live ? 1.0f / ltot : 0.0f;
+  const float inv = live ? 1.0f / lhtot : 0.0f;
   if (!row_ok) return;
   const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
   if (p.out.mode == kOutFinal) {
@@ -330,10 +379,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * db + 8 * r4 + 4 * h;
-        __bf16 v0 = (__bf16)(oacc[db][4 * r4 + 0] * inv);
-        __bf16 v1 = (__bf16)(oacc[db][4 * r4 + 1] * inv);
-        __bf16 v2 = (__bf16)(oacc[db][4 * r4 + 2] * inv);
-        __bf16 v3 = (__bf16)(oacc[db][4 * r4 + 3] * inv);
+        const __bf16 v0 = (__bf16)(oacc[db][4 * r4 + 0] * inv);
+        const __bf16 v1 = (__bf16)(oacc[db][4 * r4 + 1] * inv);
+        const __bf16 v2 = (__bf16)(oacc[db][4 * r4 + 2] * inv);
+        const __bf16 v3 = (__bf16)(oacc[db][4 * r4 + 3] * inv);
         uint2 w;
         w.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
@@ -349,22 +398,25 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * db + 8 * r4 + 4 * h;
-        float4 w = make_float4(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv,
-                               oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        *(float4*)(orow + d0) = w;
+        *(float4*)(orow + d0) = make_float4(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv,
+                                            oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
       }
     if (h == 0) {
-      p.out.pm[base] = live ? m2 * kLn2 : -INFINITY;
-      p.out.pl[base] = ltot;
+      // export the exact max: l is re-referenced from m2 to it
+      p.out.pm[base] = live ? mtrue * kLn2 : -INFINITY;
+      p.out.pl[base] = live ? ltot * __builtin_amdgcn_exp2f(m2 - mtrue) : 0.0f;
     }
   }
 }
 
+// Launch shapes: NW waves per workgroup (each 32 packed rows), TK keys per
+// tile, NS ring stages.
 template <int D, int NW>
 hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream) {
-  constexpr int STAGE = NW == 1 ? 32 : 64;
+  constexpr int TK = NW == 1 ? 32 : 64;
+  constexpr int NS = 4;
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, STAGE, NW>), grid, dim3(64 * NW), 0, stream, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -373,11 +425,7 @@ hipError_t launch_d(const AttnParams& p, int waves, hipStream_t stream) {
   switch (waves) {
     case 1: return launch_d_nw<D, 1>(p, stream);
     case 2: return launch_d_nw<D, 2>(p, stream);
-    case 3: return launch_d_nw<D, 3>(p, stream);
     case 4: return launch_d_nw<D, 4>(p, stream);
-    case 5: return launch_d_nw<D, 5>(p, stream);
-    case 6: return launch_d_nw<D, 6>(p, stream);
-    case 7: return launch_d_nw<D, 7>(p, stream);
     case 8: return launch_d_nw<D, 8>(p, stream);
     default: return hipErrorInvalidValue;
   }
@@ -386,6 +434,17 @@ hipError_t launch_d(const AttnParams& p, int waves, hipStream_t stream) {
 }  // namespace
 
 int bf16_tile_keys(int waves) { return waves == 1 ? 32 : 64; }
+
+int bf16_waves_for_rows(int64_t rows) {
+  if (rows <= 32) return 1;
+  if (rows <= 64) return 2;
+  if (rows <= 128) return 4;
+  return 8;
+}
+
+int bf16_workgroups_per_cu(int waves) { return waves >= 4 ? 1 : 2; }
+
+int bf16_index_cap() { return kIdxCap; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream) {
   if (p.head_dim == 128) return launch_d<128>(p, waves, stream);

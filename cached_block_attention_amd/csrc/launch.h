@@ -96,7 +96,12 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,
                              hipStream_t stream);
 
-// Tile keys the bf16 kernel stages per step for a given wave count.
+// Launch shape of the bf16 kernel: waves per workgroup for a chunk of packed
+// rows (1, 2, 4 or 8), keys per staged tile, workgroups resident per CU, and
+// the most retained-row indices one key split may stage.
+int bf16_waves_for_rows(int64_t rows);
 int bf16_tile_keys(int waves);
+int bf16_workgroups_per_cu(int waves);
+int bf16_index_cap();
 
 }  // namespace blkattn

@@ -57,3 +57,20 @@ def max_err(a, b, mask=None) -> float:
 
 def lse_of(m, l):
     return oracle.finalize(np.asarray(m, np.float64), np.asarray(l, np.float64))
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def worst(got, ref, mask=None):
+    """(max abs error, reference value there) for diagnostics."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    if mask is not None:
+        d = np.where(mask, d, -1.0)
+    i = np.unravel_index(int(np.argmax(d)), d.shape)
+    return float(d[i]), float(ref[i]), tuple(int(x) for x in i)

@@ -86,11 +86,12 @@ def test_degenerate_sizes_are_noops(lib):
 
 
 def test_split_plan_is_a_function_of_dims(lib):
-    # the metric workload: 16 (batch, kv-head) groups -> 32 key splits of ~16 tiles
+    # the metric workload: 16 (batch, kv-head) groups x 16 key splits = one
+    # 8-wave workgroup per compute unit, ~32 tiles of 64 keys each
     d = dims()
-    assert lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_FULL) == 32
+    assert lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_FULL) == 16
     rows = 4 * 28 * 32
-    assert lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL) >= 32 * rows * (128 + 2) * 4
+    assert lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL) >= 16 * rows * (128 + 2) * 4
     d1 = dims(splits=1)
     assert lib.blkattn_plan_splits(ctypes.byref(d1), ba.OP_FULL) == 1
     assert lib.blkattn_workspace_bytes(ctypes.byref(d1), ba.OP_FULL) == 0
@@ -98,6 +99,9 @@ def test_split_plan_is_a_function_of_dims(lib):
     assert lib.blkattn_plan_splits(ctypes.byref(tiny), ba.OP_FULL) == 1
     huge = dims(splits=100000)
     assert lib.blkattn_plan_splits(ctypes.byref(huge), ba.OP_FULL) == (32768 + 32 + 63) // 64
+    # an indexed prefix stages at most 2048 indices per split
+    sparse = dims(batch=2, prefix_len=131072, n_keep=100000, block_len=64, splits=1)
+    assert lib.blkattn_plan_splits(ctypes.byref(sparse), ba.OP_FULL) >= (100000 + 64) // 2048
 
 
 def test_binding_refuses_cpu_tensors():

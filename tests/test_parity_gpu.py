@@ -13,7 +13,7 @@ import pytest
 
 import datagen
 import oracle
-from tests.gpu_util import TOL, bits, down, lse_of, max_err, say, up
+from tests.gpu_util import TOL, bits, down, lse_of, max_err, say, up, worst
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def check_full(ba, sh, splits=0, heads=None, seed_base=None):
     tol = TOL[sh.dtype]
     eo = max_err(down(o), o_ref, mask[..., None].repeat(o_ref.shape[-1], -1))
     el = max_err(down(lse), lse_ref, mask)
-    say(f"  max err O {eo:.3e} LSE {el:.3e}")
+    say(f"  max err O {eo:.3e} LSE {el:.3e}; worst O element {worst(down(o), o_ref, mask[..., None].repeat(o_ref.shape[-1], -1))}")
     assert eo <= tol["o"] and el <= tol["lse"], (eo, el)
     return o, lse
 

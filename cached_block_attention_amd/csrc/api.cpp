@@ -112,7 +112,7 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
     pl.row_chunks = R > 256 ? (int)((R + 255) / 256) : 1;
     const int64_t rows = (R + pl.row_chunks - 1) / pl.row_chunks;
     pl.waves = bf16_waves_for_rows(rows);
-    pl.rows_per_wg = 32 * pl.waves;
+    pl.rows_per_wg = (int)(32 * ((rows + 31) / 32));  // whole 32-row waves per chunk
     pl.tile_keys = bf16_tile_keys(pl.waves);
     base = (int64_t)d->batch * d->kv_heads * pl.row_chunks;
     per_cu = bf16_workgroups_per_cu(pl.waves);

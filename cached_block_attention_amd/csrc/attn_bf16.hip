@@ -181,8 +181,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
 
   // ---- query fragment (B operand of S^T = K Q^T), resident for the loop ----
   const int prow = rc * p.rows_per_wg + wave * 32 + n;  // packed row of this lane
-  const bool row_ok = prow < R;
-  const bool computes = rc * p.rows_per_wg + wave * 32 < R;  // wave-uniform
+  const bool computes = wave * 32 < p.rows_per_wg && rc * p.rows_per_wg + wave * 32 < R;  // wave-uniform
+  const bool row_ok = computes && prow < R;
   int g = 0, qi = 0;
   if (row_ok) {
     g = prow / p.block_len;

@@ -22,7 +22,10 @@ namespace {
 // One thread merges 4 consecutive head-dim values of one row; D/4 threads of
 // the same wave share a row, so a row's m and l are read by all of its lanes in
 // the same instruction, before any lane writes them (safe in-place update).
-template <int D>
+// The partials are consumed in chunks of CH: all loads of a chunk are issued
+// before any is used, then folded into a running (M, L, acc) with the merge
+// formula, in fixed split order.
+template <int D, int CH>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
@@ -31,31 +34,53 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
 
-  auto src_o = [&](int s) -> const float* {
-    return p.strided ? p.src_o[0] + ((int64_t)s * p.split_rows + row) * D : p.src_o[s] + row * D;
-  };
-  auto src_m = [&](int s) -> float {
-    return p.strided ? p.src_m[0][(int64_t)s * p.split_rows + row] : p.src_m[s][row];
-  };
-  auto src_l = [&](int s) -> float {
-    return p.strided ? p.src_l[0][(int64_t)s * p.split_rows + row] : p.src_l[s][row];
-  };
-
   float M = -INFINITY;
-  for (int s = 0; s < p.nsrc; ++s) M = fmaxf(M, src_m(s));
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.nsrc; ++s) {
-      const float ms = src_m(s);
-      const float w = (ms == -INFINITY) ? 0.0f : src_l(s) * expf(ms - M);
-      const float4 os = *(const float4*)(src_o(s) + 4 * c4);
-      L += w;
-      acc.x = fmaf(w, os.x, acc.x);
-      acc.y = fmaf(w, os.y, acc.y);
-      acc.z = fmaf(w, os.z, acc.z);
-      acc.w = fmaf(w, os.w, acc.w);
+  for (int s0 = 0; s0 < p.nsrc; s0 += CH) {
+    float ms[CH], ls[CH];
+    float4 os[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int s = s0 + i;
+      ms[i] = -INFINITY;
+      ls[i] = 0.0f;
+      os[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < p.nsrc) {
+        const float* po;
+        if (p.strided) {
+          const int64_t e = (int64_t)s * p.split_rows + row;
+          ms[i] = p.src_m[0][e];
+          ls[i] = p.src_l[0][e];
+          po = p.src_o[0] + e * D;
+        } else {
+          const int si = s < 2 ? s : 1;  // two explicit sources
+          ms[i] = p.src_m[si][row];
+          ls[i] = p.src_l[si][row];
+          po = p.src_o[si] + row * D;
+        }
+        os[i] = *(const float4*)(po + 4 * c4);
+      }
     }
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) mc = fmaxf(mc, ms[i]);
+    if (mc == -INFINITY) continue;  // every partial so far is empty
+    if (M != -INFINITY) {
+      const float sc = expf(M - mc);
+      L *= sc;
+      acc.x *= sc, acc.y *= sc, acc.z *= sc, acc.w *= sc;
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float w = (ms[i] == -INFINITY) ? 0.0f : ls[i] * expf(ms[i] - mc);
+      L += w;
+      acc.x = fmaf(w, os[i].x, acc.x);
+      acc.y = fmaf(w, os[i].y, acc.y);
+      acc.z = fmaf(w, os[i].z, acc.z);
+      acc.w = fmaf(w, os[i].w, acc.w);
+    }
+    M = mc;
   }
   const bool live = L > 0.0f;
   const float inv = live ? 1.0f / L : 0.0f;
@@ -129,10 +154,10 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (p.head_dim == 128) {
     const int64_t blocks = (rows + 7) / 8;
-    hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<128, 8>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else if (p.head_dim == 64) {
     const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<64, 8>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -59,6 +59,24 @@ def algorithmic(sh: datagen.Shape, with_block: bool = True):
                 unit_bytes=(kv + q + idx) / (B * Hkv))
 
 
+def measured_traffic(path, sh: datagen.Shape, fn_path: str):
+    """HBM bytes per attention-kernel launch from the committed counter record
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the record
+    is for another workload or the kernel source changed since it was taken."""
+    import hashlib
+    if not path or not os.path.exists(path) or sh.name != "dream_gqa" or fn_path != "full":
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec.get("kernel_source", ""))
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
+            return None
+    return rec.get("bytes_per_launch")
+
+
 def up(x, torch):
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
@@ -109,8 +127,9 @@ def main():
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per attention-kernel launch")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_bf16_dream_gqa_traffic.json"),
+                    help="JSON record of the attention kernel's measured HBM bytes per launch "
+                         "(used only while its kernel-source hash matches the current source)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -188,10 +207,7 @@ def main():
     full_alg = algorithmic(sh)
     tflops = full_alg["flops"] / (ms_step * 1e-3) / 1e12
     achieved = alg["kernel_bytes"] / (k_ms * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic, sh, args.path)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -97,6 +97,7 @@ def library() -> ctypes.CDLL:
         "blkattn_full": (ctypes.c_int, [pd, pt, pt, pt, vp, pt, pt, pt, vp, vp, sz, vp]),
         "blkattn_prefix_partial": (ctypes.c_int, [pd, pt, pt, pt, vp, pp, vp, sz, vp]),
         "blkattn_block_partial": (ctypes.c_int, [pd, pt, pt, pt, pp, vp]),
+        "blkattn_block_step": (ctypes.c_int, [pd, pt, pt, pt, pp, pt, vp, vp]),
         "blkattn_merge": (ctypes.c_int, [pd, pp, pp, pt, vp, pp, vp]),
         "blkattn_gather_prefix": (ctypes.c_int, [pd, pt, pt, vp, pt, pt, vp]),
         "blkattn_workspace_bytes": (ctypes.c_size_t, [pd, ctypes.c_int]),
@@ -270,6 +271,18 @@ def blkattn_block_partial(q, k_blk, v_blk, out: Partial, scale=None, stream=None
     return out
 
 
+def blkattn_block_step(q, k_blk, v_blk, cached: Partial, o, lse=None, scale=None, stream=None):
+    """One reuse step in one launch: the block queries' state starts from the cached
+    prefix partial and continues over the block's own keys; writes O and LSE."""
+    _check_gpu(q, k_blk, v_blk, *cached, o, lse)
+    dims = make_dims(q, k_blk.shape[1], 0, 0, scale, 0)
+    st = library().blkattn_block_step(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_blk)),
+                                      _ref(_tensor(v_blk)), _ref(_partial(cached)), _ref(_tensor(o)),
+                                      _ptr(lse), _stream(stream))
+    _raise(st)
+    return o, lse
+
+
 def blkattn_merge(a: Partial, b: Partial, o=None, lse=None, ab: Optional[Partial] = None,
                   dtype=None, stream=None):
     """Log-sum-exp merge of two partials; writes O (dtype of `o`), LSE and/or `ab`."""
@@ -320,6 +333,15 @@ def block_partial(q, k_blk, v_blk, scale=None, stream=None) -> Partial:
     B, Hq, Bq, d = q.shape
     out = empty_partial(B, Hq, Bq, d, q.device)
     return blkattn_block_partial(q, k_blk, v_blk, out, scale=scale, stream=stream)
+
+
+def block_step(q, k_blk, v_blk, cached: Partial, scale=None, stream=None):
+    """Allocate O and LSE and run blkattn_block_step."""
+    torch = _torch()
+    B, Hq, Bq, d = q.shape
+    o = torch.empty(B, Hq, Bq, d, dtype=q.dtype, device=q.device)
+    lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device=q.device)
+    return blkattn_block_step(q, k_blk, v_blk, cached, o, lse, scale=scale, stream=stream)
 
 
 def merge(a: Partial, b: Partial, dtype=None, stream=None):

@@ -413,6 +413,37 @@ int blkattn_block_partial(const blkattn_dims* d, const blkattn_tensor* q, const 
   return ok();
 }
 
+int blkattn_block_step(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_blk,
+                       const blkattn_tensor* v_blk, const blkattn_partial* cached, const blkattn_tensor* o,
+                       float* lse, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if ((st = check_tensor(k_blk, "k_blk", eb, 1))) return st;
+  if ((st = check_tensor(v_blk, "v_blk", eb, 1))) return st;
+  if ((st = check_partial(cached, "cached", rows))) return st;
+  if ((st = check_tensor(o, "o", eb, 1))) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  blkattn_dims d1 = *d;
+  d1.splits = 1;  // the block's keys in one split, continuing the cached state
+  const Plan pl = make_plan(&d1, d->block_len, false);
+  AttnParams p = attn_params(&d1, q, pl);
+  fill_keys(p.keys, &d1, nullptr, nullptr, nullptr, k_blk, v_blk, 0, d->block_len);
+  p.init_o = cached->o, p.init_m = cached->m, p.init_l = cached->l;
+  p.out.mode = kOutFinal;
+  p.out.o = o->data;
+  p.out.o_sb = o->stride_b, p.out.o_sh = o->stride_h, p.out.o_st = o->stride_t;
+  p.out.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = d->dtype == BLKATTN_F32 ? launch_attn_f32(p, s) : launch_attn_bf16(p, pl.waves, s);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int blkattn_merge(const blkattn_dims* d, const blkattn_partial* a, const blkattn_partial* b,
                   const blkattn_tensor* o, float* lse, const blkattn_partial* ab, void* stream) {
   int st = check_dims(d);

@@ -51,6 +51,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kSlack = 8.0f;  // log2 of the largest unnormalised weight allowed
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -254,6 +255,31 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   float lsum = 0.0f;        // lane-partial sum of weights
   float lhat = 0.0f;        // lane-partial sum of the bf16-rounded weights
   const float c2 = p.scale_log2;
+  // Initial state from a cached partial (LaCache Appendix J: the running
+  // (m, l, O~) of a later step starts from the cache): O~ = l * o, m in base 2,
+  // l carried by the lanes of the first wave half.
+  if (p.init_m != nullptr && row_ok) {
+    const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
+    const float mi = p.init_m[prow_flat];
+    const float li = p.init_l[prow_flat];
+    if (mi > -INFINITY && li > 0.0f) {
+      m2 = mi * kLog2e;
+      mtrue = m2;
+      lsum = h == 0 ? li : 0.0f;
+      lhat = lsum;
+      const float* orow = p.init_o + prow_flat * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 v = *(const float4*)(orow + 32 * db + 8 * r4 + 4 * h);
+          oacc[db][4 * r4 + 0] = v.x * li;
+          oacc[db][4 * r4 + 1] = v.y * li;
+          oacc[db][4 * r4 + 2] = v.z * li;
+          oacc[db][4 * r4 + 3] = v.w * li;
+        }
+    }
+  }
 
   wait_vm<0>();  // the query fragment has landed before any DMA is counted
   const int npro = nst < NS - 1 ? nst : NS - 1;

@@ -59,6 +59,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
       o[d] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
+    if (p.init_m != nullptr && ok) {
+      // initial state from a cached partial: O~ = l * o (LaCache Appendix J)
+      const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
+      const float mi = p.init_m[prow_flat];
+      const float li = p.init_l[prow_flat];
+      if (mi > -INFINITY && li > 0.0f) {
+        m = mi;
+        l = li;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] = p.init_o[prow_flat * D + d] * li;
+      }
+    }
     for (int t = t0; t < t1; ++t) {
       const int64_t key0 = (int64_t)t * kF32Tile;
       const int64_t rem = N - key0;

@@ -56,6 +56,12 @@ struct AttnParams {
   int32_t tiles;        // ceil((n_pre + n_blk) / tile keys of this kernel)
   int32_t rows_per_wg;  // packed (q-head, query) rows one workgroup owns
   int32_t row_chunks;   // workgroups along the packed rows of one kv-head
+  // Optional initial state (one key split only): contiguous fp32 partial
+  // (o [rows, d], m, l [rows]) the running state starts from instead of the
+  // empty state; nullptr when absent.
+  const float* init_o;
+  const float* init_m;
+  const float* init_l;
 };
 
 // Inputs of an N-way log-sum-exp merge of partials (same rows, disjoint keys).

@@ -169,6 +169,26 @@ int blkattn_block_partial(const blkattn_dims* dims, const blkattn_tensor* q,
                           const blkattn_partial* out, void* stream);
 
 /*
+ * blkattn_block_step - one denoising step of the reuse path in one launch:
+ * every block query's running online-softmax state starts from the cached
+ * prefix partial and continues over the block's own Bq keys (no mask), then
+ * O and LSE are finalised. This is LaCache's initialisation of (m, l, O~) from
+ * the cache followed by the recurrence over the tiles of the current block
+ * (section 3.3.3 eqs. 2-6 and the Appendix J pseudocode); it equals
+ * blkattn_block_partial followed by blkattn_merge with the cached partial, up
+ * to rounding, without the block partial passing through memory.
+ *   q [B, Hq, Bq, d]; k_blk, v_blk [B, Hkv, Bq, d]
+ *   cached  contiguous fp32 partial [B, Hq, Bq, (d)] of the same queries over
+ *           the prefix (read only; an empty state is allowed)
+ *   o       [B, Hq, Bq, d] output in dims->dtype; must not alias an input
+ *   lse     fp32 [B, Hq, Bq], or NULL
+ * prefix_len, n_keep and splits are ignored.
+ */
+int blkattn_block_step(const blkattn_dims* dims, const blkattn_tensor* q, const blkattn_tensor* k_blk,
+                       const blkattn_tensor* v_blk, const blkattn_partial* cached,
+                       const blkattn_tensor* o, float* lse, void* stream);
+
+/*
  * blkattn_merge - log-sum-exp merge of two partial states of the same queries
  * over disjoint key sets: M = max(m_a, m_b), w_x = l_x e^{m_x - M},
  * l = w_a + w_b, o = (w_a o_a + w_b o_b) / l, LSE = M + ln l. Continuing the

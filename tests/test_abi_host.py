@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = header_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -83,6 +83,24 @@ def test_degenerate_sizes_are_noops(lib):
         d = dims(**kw)
         assert lib.blkattn_full(ctypes.byref(d), None, None, None, None, None, None, None, None,
                                 None, 0, None) == ba.OK
+
+
+def test_block_step_rejects_before_launch(lib):
+    d = dims()
+    t = ba.Tensor(4096, 128 * 32, 128 * 32, 128)
+    good = ba.PartialDesc(8192, 4096, 4096)
+
+    def call(cached, o=t, lse=None, dd=d):
+        return lib.blkattn_block_step(ctypes.byref(dd), ctypes.byref(t), ctypes.byref(t), ctypes.byref(t),
+                                      None if cached is None else ctypes.byref(cached),
+                                      None if o is None else ctypes.byref(o), lse, None)
+    assert call(None) == ba.ERR_INVALID_ARG                                   # no cached partial
+    assert call(ba.PartialDesc(8192, None, 4096)) == ba.ERR_INVALID_ARG        # cached.m missing
+    assert call(ba.PartialDesc(8200, 4096, 4096)) == ba.ERR_MISALIGNED         # cached.o not 16 B aligned
+    assert call(good, o=None) == ba.ERR_INVALID_ARG                          # no output
+    assert call(good, lse=4098) == ba.ERR_MISALIGNED
+    assert call(good, dd=dims(head_dim=80)) == ba.ERR_UNSUPPORTED
+    assert call(None, o=None, dd=dims(block_len=0)) == ba.OK                   # empty block: no-op
 
 
 def test_split_plan_is_a_function_of_dims(lib):

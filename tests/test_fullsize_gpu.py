@@ -101,6 +101,7 @@ def test_reuse_eight_steps_sampled(ba):
         qt, kb, vb = up(qt_np), up(kb_np), up(vb_np)
         pb = ba.block_partial(qt, kb, vb)
         o, lse = ba.merge(pp, pb, dtype=torch.bfloat16)
+        so, slse = ba.block_step(qt, kb, vb, pp)   # the same step in one launch
         torch.cuda.synchronize()
         for b, h in heads:
             rb = oracle.partial(qt_np[b:b + 1, h:h + 1], kb_np[b:b + 1, h:h + 1], vb_np[b:b + 1, h:h + 1],
@@ -108,6 +109,8 @@ def test_reuse_eight_steps_sampled(ba):
             ro, rm, rl, rlse = oracle.merge(ref_pp[(b, h)], rb)
             assert max_err(down(o[b, h]), ro[0, 0]) <= tol["o"], (t, b, h)
             assert max_err(down(lse[b, h]), rlse[0, 0]) <= tol["lse"], (t, b, h)
+            assert max_err(down(so[b, h]), ro[0, 0]) <= tol["o"], (t, b, h)
+            assert max_err(down(slse[b, h]), rlse[0, 0]) <= tol["lse"], (t, b, h)
             if t == 0:
                 fo, fl = oracle.full(inp.q[b:b + 1, h:h + 1], inp.k_pre[b:b + 1, h:h + 1],
                                      inp.v_pre[b:b + 1, h:h + 1], inp.k_blk[b:b + 1, h:h + 1],

@@ -200,6 +200,60 @@ def test_prefix_block_partials_and_merge(ba, name, kw, splits):
     assert max_err(lse_of(down(pp.m), down(pp.l)), rlse) <= TOL[sh.dtype]["lse"]
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {}),
+    ("dream_gqa", dict(batch=2, prefix_len=1500)),
+    ("dream_gqa", dict(batch=1, q_heads=14, kv_heads=2, prefix_len=700, block_len=64)),
+    ("llada_bf16", dict(q_heads=4, kv_heads=4, prefix_len=900)),
+    ("sparse_gqa", dict(prefix_len=2000, n_keep=333)),
+    ("dream_gqa", dict(batch=1, q_heads=6, kv_heads=2, prefix_len=300, block_len=20, head_dim=64)),
+])
+def test_block_step_continues_the_cached_state(ba, name, kw):
+    # one launch: state initialised from the cached prefix partial, continued
+    # over the block keys == full attention (same queries) == partial + merge
+    import torch
+    sh = datagen.scaled_shape(name, **kw)
+    say(f"case block step {sh}")
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"], idx=t["idx"])
+    o, lse = ba.block_step(t["q"], t["k_blk"], t["v_blk"], pp)
+    pb = ba.block_partial(t["q"], t["k_blk"], t["v_blk"])
+    o2, lse2 = ba.merge(pp, pb, dtype=t["q"].dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=inp.idx)
+    tol = TOL[sh.dtype]
+    eo, el = max_err(down(o), o_ref), max_err(down(lse), lse_ref)
+    say(f"  block step err O {eo:.3e} LSE {el:.3e}")
+    assert eo <= tol["o"] and el <= tol["lse"], (eo, el)
+    assert max_err(down(o), down(o2)) <= tol["o"] and max_err(down(lse), down(lse2)) <= tol["lse"]
+
+
+def test_block_step_from_empty_and_from_other_queries(ba):
+    import torch
+    sh = shape(batch=1, q_heads=8, kv_heads=2, prefix_len=400, block_len=32)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    # an empty cached state gives block-only attention
+    empty = ba.empty_partial(1, 8, 32, 128, "cuda")
+    empty.o.zero_()
+    empty.m.fill_(-float("inf"))
+    empty.l.zero_()
+    o, lse = ba.block_step(t["q"], t["k_blk"], t["v_blk"], empty)
+    torch.cuda.synchronize()
+    bo, bl = oracle.full(inp.q, inp.k_pre[:, :, :0], inp.v_pre[:, :, :0], inp.k_blk, inp.v_blk, sh.scale)
+    assert max_err(down(o), bo) <= TOL["bf16"]["o"] and max_err(down(lse), bl) <= TOL["bf16"]["lse"]
+    # a state cached from other (step-0) queries, continued with fresh block
+    # queries: the composition merge(partial(Q_fix; prefix), partial(Q_t; block))
+    q1_np, kb_np, vb_np = datagen.step_inputs(sh, 1)
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"])
+    o, lse = ba.block_step(up(q1_np), up(kb_np), up(vb_np), pp)
+    torch.cuda.synchronize()
+    ro, rm, rl, rlse = oracle.merge(oracle.partial(inp.q, inp.k_pre, inp.v_pre, sh.scale),
+                                    oracle.partial(q1_np, kb_np, vb_np, sh.scale))
+    assert max_err(down(o), ro) <= TOL["bf16"]["o"] and max_err(down(lse), rlse) <= TOL["bf16"]["lse"]
+
+
 def test_empty_prefix_partial_and_merges(ba):
     import torch
     sh = shape(batch=1, q_heads=4, kv_heads=2, prefix_len=0, block_len=32)

@@ -100,6 +100,8 @@ def library() -> ctypes.CDLL:
         "blkattn_block_step": (ctypes.c_int, [pd, pt, pt, pt, pp, pt, vp, vp]),
         "blkattn_merge": (ctypes.c_int, [pd, pp, pp, pt, vp, pp, vp]),
         "blkattn_gather_prefix": (ctypes.c_int, [pd, pt, pt, vp, pt, pt, vp]),
+        "blkattn_prefix_mass": (ctypes.c_int, [pd, pt, pt, vp, vp, vp]),
+        "blkattn_select_retained": (ctypes.c_int, [pd, vp, vp, vp]),
         "blkattn_workspace_bytes": (ctypes.c_size_t, [pd, ctypes.c_int]),
         "blkattn_plan_splits": (ctypes.c_int, [pd, ctypes.c_int]),
         "blkattn_set_kernel_events": (None, [vp, vp]),
@@ -309,6 +311,27 @@ def blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=None):
     return k_out, v_out
 
 
+def blkattn_prefix_mass(q, k_pre, lse, mass, scale=None, stream=None):
+    """Attention mass of every prefix row (summed probabilities over the block
+    queries of the kv group), given each row's LSE over all keys."""
+    _check_gpu(q, k_pre, lse, mass)
+    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], 0, scale, 0)
+    st = library().blkattn_prefix_mass(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
+                                       _ptr(lse), _ptr(mass), _stream(stream))
+    _raise(st)
+    return mass
+
+
+def blkattn_select_retained(mass, idx, stream=None):
+    """The idx.shape[-1] rows of largest mass per (batch, kv head), ascending."""
+    _check_gpu(mass, idx)
+    B, Hkv, P = mass.shape
+    dims = Dims(B, Hkv, Hkv, 64, 1, int(idx.shape[-1]), P, F32, 1.0, 0, 0)
+    st = library().blkattn_select_retained(ctypes.byref(dims), _ptr(mass), _ptr(idx), _stream(stream))
+    _raise(st)
+    return idx
+
+
 # ---------------------------------------------------------------------------
 # allocating conveniences (device memory from torch, compute in the library)
 # ---------------------------------------------------------------------------
@@ -353,6 +376,20 @@ def merge(a: Partial, b: Partial, dtype=None, stream=None):
     lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device=a.o.device)
     blkattn_merge(a, b, o=o, lse=lse, stream=stream)
     return o, lse
+
+
+def prefix_mass(q, k_pre, lse, scale=None, stream=None):
+    torch = _torch()
+    B, Hkv, P, _ = k_pre.shape
+    mass = torch.empty(B, Hkv, P, dtype=torch.float32, device=q.device)
+    return blkattn_prefix_mass(q, k_pre, lse, mass, scale=scale, stream=stream)
+
+
+def select_retained(mass, n_keep: int, stream=None):
+    torch = _torch()
+    B, Hkv, _ = mass.shape
+    idx = torch.empty(B, Hkv, n_keep, dtype=torch.int32, device=mass.device)
+    return blkattn_select_retained(mass, idx, stream=stream)
 
 
 def gather_prefix(k_full, v_full, idx, stream=None):

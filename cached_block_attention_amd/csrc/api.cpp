@@ -475,6 +475,61 @@ int blkattn_merge(const blkattn_dims* d, const blkattn_partial* a, const blkattn
   return ok();
 }
 
+int blkattn_prefix_mass(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                        const float* lse, float* mass, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int eb = elt_bytes(d->dtype);
+  if (d->batch == 0 || d->prefix_len == 0) return ok();
+  if ((st = check_tensor(k_pre, "k_pre", eb, 1))) return st;
+  if (mass == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "mass is NULL");
+  if (reinterpret_cast<uintptr_t>(mass) % 4 != 0) return fail(BLKATTN_ERR_MISALIGNED, "mass is not 4-byte aligned");
+  const int64_t groups = (int64_t)d->batch * d->kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  if (d->q_heads == 0 || d->block_len == 0) return ok();  // degenerate: no-op
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if (lse == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  const int64_t R = (int64_t)(d->q_heads / d->kv_heads) * d->block_len;
+  if (d->dtype == BLKATTN_BF16 && R > mass_max_rows())
+    return fail(BLKATTN_ERR_UNSUPPORTED, "q_heads/kv_heads * block_len = %lld exceeds %d rows per kv head",
+                (long long)R, mass_max_rows());
+  MassParams p{};
+  p.batch = d->batch, p.q_heads = d->q_heads, p.kv_heads = d->kv_heads, p.group = d->q_heads / d->kv_heads;
+  p.head_dim = d->head_dim, p.block_len = d->block_len, p.dtype = d->dtype;
+  p.q = q->data, p.q_sb = q->stride_b, p.q_sh = q->stride_h, p.q_st = q->stride_t;
+  p.k = k_pre->data, p.k_sb = k_pre->stride_b, p.k_sh = k_pre->stride_h, p.k_st = k_pre->stride_t;
+  p.n_keys = d->prefix_len;
+  p.lse = lse, p.mass = mass;
+  p.scale = d->scale;
+  p.scale_log2 = (float)((double)d->scale * 1.4426950408889634);
+  p.tiles = (int)((d->prefix_len + mass_tile_keys() - 1) / mass_tile_keys());
+  int64_t splits = (kComputeUnits + groups - 1) / groups;
+  if (splits > p.tiles) splits = p.tiles;
+  if (splits < 1) splits = 1;
+  p.splits = (int)splits;
+  hipError_t e = launch_mass(p, s);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "mass kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int blkattn_select_retained(const blkattn_dims* d, const float* mass, int32_t* idx, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (d->batch == 0 || d->n_keep == 0) return ok();
+  if (d->n_keep > d->prefix_len)
+    return fail(BLKATTN_ERR_INVALID_ARG, "n_keep (%d) exceeds prefix_len (%lld)", d->n_keep,
+                (long long)d->prefix_len);
+  if (d->prefix_len > INT32_MAX) return fail(BLKATTN_ERR_UNSUPPORTED, "prefix_len does not fit int32 indices");
+  if (mass == nullptr || idx == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "mass or idx is NULL");
+  if (reinterpret_cast<uintptr_t>(mass) % 4 != 0 || reinterpret_cast<uintptr_t>(idx) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "mass and idx must be 4-byte aligned");
+  hipError_t e = launch_select(mass, idx, (int64_t)d->batch * d->kv_heads, d->prefix_len, d->n_keep,
+                               (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int blkattn_gather_prefix(const blkattn_dims* d, const blkattn_tensor* k_full, const blkattn_tensor* v_full,
                           const int32_t* idx, const blkattn_tensor* k_out, const blkattn_tensor* v_out,
                           void* stream) {

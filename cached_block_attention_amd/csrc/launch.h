@@ -94,6 +94,23 @@ struct GatherParams {
   int64_t ko_sb, ko_sh, ko_st, vo_sb, vo_sh, vo_st;
 };
 
+// Attention mass of the dense prefix keys (see mass_topk.hip).
+struct MassParams {
+  int32_t batch, q_heads, kv_heads, group, head_dim, block_len;
+  int32_t dtype;                // BLKATTN_F32 / BLKATTN_BF16
+  const void* q;
+  int64_t q_sb, q_sh, q_st;
+  const void* k;                // prefix keys [B, Hkv, n_keys, d]
+  int64_t k_sb, k_sh, k_st;
+  int64_t n_keys;
+  const float* lse;             // [B, Hq, Bq] row log-sum-exp over all keys
+  float* mass;                  // [B, Hkv, n_keys]
+  float scale;
+  float scale_log2;
+  int32_t splits;               // bf16: key splits (gridDim.x)
+  int32_t tiles;                // bf16: ceil(n_keys / mass_tile_keys())
+};
+
 // Kernel launchers (return the hipError_t of the launch).
 hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
@@ -101,6 +118,11 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,
                              hipStream_t stream);
+hipError_t launch_mass(const MassParams& p, hipStream_t stream);
+hipError_t launch_select(const float* mass, int32_t* idx, int64_t groups, int64_t n, int64_t k,
+                         hipStream_t stream);
+int mass_max_rows();   // largest G * Bq the bf16 mass kernel supports
+int mass_tile_keys();  // keys per tile of the bf16 mass kernel
 
 // Launch shape of the bf16 kernel: waves per workgroup for a chunk of packed
 // rows (1, 2, 4 or 8), keys per staged tile, workgroups resident per CU, and

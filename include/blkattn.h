@@ -218,6 +218,35 @@ int blkattn_gather_prefix(const blkattn_dims* dims, const blkattn_tensor* k_full
                           const blkattn_tensor* v_full, const int32_t* idx,
                           const blkattn_tensor* k_out, const blkattn_tensor* v_out, void* stream);
 
+/*
+ * blkattn_prefix_mass - attention mass of every dense prefix row:
+ *   mass[b, h, j] = sum over the q-heads g of kv head h and the block queries i
+ *                   of exp(scale * <q[b, g, i], k_pre[b, h, j]> - lse[b, g, i])
+ * i.e. the attention probability key j receives, summed over the queries that
+ * read it; the score that guides which prefix rows to retain (Sparse-dLLM
+ * abstract on the aitopics "kv state" page: keep the critical tokens, evict
+ * the rest).
+ *   q      [B, Hq, Bq, d]
+ *   k_pre  [B, Hkv, prefix_len, d] (dense: n_keep and indices play no part)
+ *   lse    fp32 [B, Hq, Bq] contiguous: each row's log-sum-exp over all keys it
+ *          attends (as blkattn_full returns it)
+ *   mass   fp32 [B, Hkv, prefix_len] contiguous output
+ * bf16 supports q_heads / kv_heads * block_len <= 1024. The column sums run in
+ * a fixed order (bitwise reproducible).
+ */
+int blkattn_prefix_mass(const blkattn_dims* dims, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                        const float* lse, float* mass, void* stream);
+
+/*
+ * blkattn_select_retained - per (batch, kv head), the n_keep prefix rows of
+ * largest mass, ties broken towards the lower row, listed in ascending row
+ * order: the index layout of blkattn_full / blkattn_gather_prefix.
+ *   mass  fp32 [B, Hkv, prefix_len] contiguous, finite and >= 0
+ *   idx   int32 [B, Hkv, n_keep] contiguous output
+ * Requires n_keep <= prefix_len. Deterministic (an exact radix selection).
+ */
+int blkattn_select_retained(const blkattn_dims* dims, const float* mass, int32_t* idx, void* stream);
+
 /* Workspace bytes blkattn_full / blkattn_prefix_partial need for these dims
  * (0 when the plan uses a single key split). The prefix is taken as indexed
  * with n_keep rows when n_keep > 0, else as prefix_len dense rows; an indexed

@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
     online_state,
     state_from_partial,
 )
+from .retention import prefix_mass, select_retained  # noqa: F401

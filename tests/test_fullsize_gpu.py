@@ -118,3 +118,35 @@ def test_reuse_eight_steps_sampled(ba):
                 assert max_err(down(o[b, h]), fo[0, 0]) <= tol["o"]
                 assert max_err(down(lse[b, h]), fl[0, 0]) <= tol["lse"]
         say(f"  reuse step {t} ok")
+
+
+def test_sparse_gqa_retention_from_attention_mass(ba):
+    """The step that produces the retained rows at the sparse workload's full
+    size: dense attention over all 131072 prefix rows and the block gives each
+    row's LSE, the attention mass of every prefix row follows, and the 8192
+    rows of largest mass are kept. Mass checked on sampled kv heads against the
+    oracle; selection bit-exact against the oracle's rule on the same masses."""
+    import torch
+    sh = datagen.WORKLOADS["sparse_gqa"]
+    say("case full-size sparse_gqa retention: generating inputs")
+    inp = datagen.make_inputs(sh)
+    q, kp, vp, kb, vb = (up(getattr(inp, k)) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk"))
+    _, lse = ba.attention(q, kp, vp, kb, vb)
+    mass = ba.prefix_mass(q, kp, lse)
+    idx = ba.select_retained(mass, sh.n_keep)
+    torch.cuda.synchronize()
+    got = down(mass)
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, oracle.select_retained(got, sh.n_keep))
+    G = sh.q_heads // sh.kv_heads
+    rows = G * sh.block_len
+    for b, h in ((0, 0), (sh.batch - 1, sh.kv_heads - 1)):
+        heads = [(b, h * G + g) for g in range(G)]
+        _, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, heads=heads)
+        ref = oracle.prefix_mass(inp.q[b:b + 1, h * G:(h + 1) * G], inp.k_pre[b:b + 1, h:h + 1],
+                                 lse_ref[b:b + 1, h * G:(h + 1) * G], sh.scale)[0, 0]
+        err = np.abs(got[b, h] - ref)
+        say(f"  mass (b={b}, kv head {h}): max err {err.max():.3e}, max mass {ref.max():.3e}")
+        assert np.all(err <= 1e-4 * np.maximum(1.0, ref) + 1e-7 * rows)
+        cut = np.sort(ref)[::-1][sh.n_keep - 1]
+        assert np.all(ref[gi[b, h]] >= cut - 2 * (1e-4 * max(1.0, cut) + 1e-7 * rows))

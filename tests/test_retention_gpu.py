@@ -1,0 +1,115 @@
+"""Parity of attention-guided retention on the GPU (blkattn_prefix_mass and
+blkattn_select_retained, through the C ABI) with the fp64 oracle.
+
+Mass: max |gpu - oracle| <= 1e-4 * max(1, oracle) + 1e-7 * (rows read) per key
+(fp32 probabilities from fp32 scores, each row's LSE from the same path).
+Selection: bit-exact against the oracle's rule applied to the same fp32
+masses; against the oracle's own masses, every kept row must rank within the
+mass tolerance of the oracle's n_keep-th largest (keys closer than that may
+trade places)."""
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from tests.gpu_util import down, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ba():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cached_block_attention_amd as mod
+    mod.library()
+    return mod
+
+
+def upload(inp):
+    return {k: up(getattr(inp, k)) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
+
+
+def mass_tol(ref, rows):
+    return 1e-4 * np.maximum(1.0, ref) + 1e-7 * rows
+
+
+CASES = [
+    ("tiny_f32", {}),
+    ("dream_gqa", dict(batch=2, prefix_len=1000)),                                   # 224 rows
+    ("sparse_gqa", dict(prefix_len=1500, n_keep=None)),                             # 448 rows
+    ("llada_bf16", dict(q_heads=3, kv_heads=3, prefix_len=700)),                    # 32 rows
+    ("dream_gqa", dict(batch=1, q_heads=6, kv_heads=2, prefix_len=333, block_len=20, head_dim=64)),
+    ("dream_gqa", dict(batch=1, q_heads=16, kv_heads=1, prefix_len=200, block_len=64)),  # 1024 rows
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=lambda x: str(x))
+def test_mass_and_selection(ba, name, kw):
+    import torch
+    sh = datagen.scaled_shape(name, **kw)
+    say(f"case retention {sh}")
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    _, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+    mass = ba.prefix_mass(t["q"], t["k_pre"], lse)
+    torch.cuda.synchronize()
+    _, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale)
+    ref = oracle.prefix_mass(inp.q, inp.k_pre, lse_ref, sh.scale)
+    got = down(mass)
+    rows = sh.q_heads // sh.kv_heads * sh.block_len
+    err = np.abs(got - ref)
+    say(f"  mass max err {err.max():.3e} (max mass {ref.max():.3e})")
+    assert np.all(err <= mass_tol(ref, rows))
+    n_keep = max(1, sh.prefix_len // 7)
+    idx = ba.select_retained(mass, n_keep)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, oracle.select_retained(got, n_keep))
+    # against the oracle's masses: kept rows are within tolerance of the cut
+    for b in range(sh.batch):
+        for h in range(sh.kv_heads):
+            cut = np.sort(ref[b, h])[::-1][n_keep - 1]
+            tol = mass_tol(cut, rows)
+            assert np.all(ref[b, h, gi[b, h]] >= cut - 2 * tol)
+    # the kept rows feed the gathered attention
+    o, lse2 = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=idx)
+    torch.cuda.synchronize()
+    o_ref, lse2_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=gi)
+    from tests.gpu_util import TOL, max_err
+    assert max_err(down(o), o_ref) <= TOL[sh.dtype]["o"] and max_err(down(lse2), lse2_ref) <= TOL[sh.dtype]["lse"]
+
+
+def test_selection_ties_and_edges(ba):
+    import torch
+    rng = np.random.default_rng(5)
+    P = 5000
+    m = rng.integers(0, 40, size=(2, 3, P)).astype(np.float32)   # heavy ties
+    m[1, 2] = 0.25                                                # all equal
+    m[0, 1, ::2] = 1e-30                                          # tiny values
+    mt = torch.from_numpy(m).cuda()
+    for k in (1, 2, 777, P - 1, P):
+        idx = ba.select_retained(mt, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oracle.select_retained(m.astype(np.float64), k)), k
+    # a large row count crossing many threads' chunks
+    big = rng.random((1, 1, 131072)).astype(np.float32)
+    big[0, 0, 1000:1100] = big[0, 0, 5]
+    bt = torch.from_numpy(big).cuda()
+    idx = ba.select_retained(bt, 8192)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.select_retained(big.astype(np.float64), 8192))
+
+
+def test_mass_is_deterministic(ba):
+    import torch
+    sh = datagen.scaled_shape("dream_gqa", batch=1, prefix_len=3000)
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    _, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+    m1 = ba.prefix_mass(t["q"], t["k_pre"], lse)
+    m2 = ba.prefix_mass(t["q"], t["k_pre"], lse)
+    torch.cuda.synchronize()
+    assert torch.equal(m1, m2)

@@ -26,6 +26,7 @@ F32 = 0
 BF16 = 1
 OP_FULL = 0
 OP_PREFIX_PARTIAL = 1
+OP_SELECT = 2
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -101,7 +102,7 @@ def library() -> ctypes.CDLL:
         "blkattn_merge": (ctypes.c_int, [pd, pp, pp, pt, vp, pp, vp]),
         "blkattn_gather_prefix": (ctypes.c_int, [pd, pt, pt, vp, pt, pt, vp]),
         "blkattn_prefix_mass": (ctypes.c_int, [pd, pt, pt, vp, vp, vp]),
-        "blkattn_select_retained": (ctypes.c_int, [pd, vp, vp, vp]),
+        "blkattn_select_retained": (ctypes.c_int, [pd, vp, vp, vp, sz, vp]),
         "blkattn_workspace_bytes": (ctypes.c_size_t, [pd, ctypes.c_int]),
         "blkattn_plan_splits": (ctypes.c_int, [pd, ctypes.c_int]),
         "blkattn_set_kernel_events": (None, [vp, vp]),
@@ -322,12 +323,14 @@ def blkattn_prefix_mass(q, k_pre, lse, mass, scale=None, stream=None):
     return mass
 
 
-def blkattn_select_retained(mass, idx, stream=None):
+def blkattn_select_retained(mass, idx, workspace=None, stream=None):
     """The idx.shape[-1] rows of largest mass per (batch, kv head), ascending."""
     _check_gpu(mass, idx)
     B, Hkv, P = mass.shape
     dims = Dims(B, Hkv, Hkv, 64, 1, int(idx.shape[-1]), P, F32, 1.0, 0, 0)
-    st = library().blkattn_select_retained(ctypes.byref(dims), _ptr(mass), _ptr(idx), _stream(stream))
+    ws, nbytes = _workspace(dims, OP_SELECT, mass.device, workspace)
+    st = library().blkattn_select_retained(ctypes.byref(dims), _ptr(mass), _ptr(idx), _ptr(ws), nbytes,
+                                           _stream(stream))
     _raise(st)
     return idx
 
@@ -385,11 +388,11 @@ def prefix_mass(q, k_pre, lse, scale=None, stream=None):
     return blkattn_prefix_mass(q, k_pre, lse, mass, scale=scale, stream=stream)
 
 
-def select_retained(mass, n_keep: int, stream=None):
+def select_retained(mass, n_keep: int, workspace=None, stream=None):
     torch = _torch()
     B, Hkv, _ = mass.shape
     idx = torch.empty(B, Hkv, n_keep, dtype=torch.int32, device=mass.device)
-    return blkattn_select_retained(mass, idx, stream=stream)
+    return blkattn_select_retained(mass, idx, workspace=workspace, stream=stream)
 
 
 def gather_prefix(k_full, v_full, idx, stream=None):

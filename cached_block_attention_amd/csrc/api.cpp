@@ -250,6 +250,7 @@ void blkattn_set_kernel_events(void* start, void* stop) {
 int blkattn_plan_splits(const blkattn_dims* d, int op) {
   int st = check_dims(d);
   if (st != BLKATTN_OK) return st;
+  if (op == BLKATTN_OP_SELECT) return select_plan((int64_t)d->batch * d->kv_heads, d->prefix_len).chunks;
   if (op != BLKATTN_OP_FULL && op != BLKATTN_OP_PREFIX_PARTIAL)
     return fail(BLKATTN_ERR_INVALID_ARG, "unknown op %d", op);
   const bool indexed = d->n_keep > 0;
@@ -261,6 +262,7 @@ int blkattn_plan_splits(const blkattn_dims* d, int op) {
 size_t blkattn_workspace_bytes(const blkattn_dims* d, int op) {
   const int s = blkattn_plan_splits(d, op);
   if (s < 1) return 0;
+  if (op == BLKATTN_OP_SELECT) return select_plan((int64_t)d->batch * d->kv_heads, d->prefix_len).ws_bytes;
   return ws_layout(d, s).total;
 }
 
@@ -513,7 +515,8 @@ int blkattn_prefix_mass(const blkattn_dims* d, const blkattn_tensor* q, const bl
   return ok();
 }
 
-int blkattn_select_retained(const blkattn_dims* d, const float* mass, int32_t* idx, void* stream) {
+int blkattn_select_retained(const blkattn_dims* d, const float* mass, int32_t* idx, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   int st = check_dims(d);
   if (st) return st;
   if (d->batch == 0 || d->n_keep == 0) return ok();
@@ -524,8 +527,16 @@ int blkattn_select_retained(const blkattn_dims* d, const float* mass, int32_t* i
   if (mass == nullptr || idx == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "mass or idx is NULL");
   if (reinterpret_cast<uintptr_t>(mass) % 4 != 0 || reinterpret_cast<uintptr_t>(idx) % 4 != 0)
     return fail(BLKATTN_ERR_MISALIGNED, "mass and idx must be 4-byte aligned");
-  hipError_t e = launch_select(mass, idx, (int64_t)d->batch * d->kv_heads, d->prefix_len, d->n_keep,
-                               (hipStream_t)stream);
+  const int64_t groups = (int64_t)d->batch * d->kv_heads;
+  const size_t need = select_plan(groups, d->prefix_len).ws_bytes;
+  if (d->n_keep < d->prefix_len) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  }
+  hipError_t e = launch_select(mass, idx, workspace, groups, d->prefix_len, d->n_keep, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -119,7 +119,15 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,
                              hipStream_t stream);
 hipError_t launch_mass(const MassParams& p, hipStream_t stream);
-hipError_t launch_select(const float* mass, int32_t* idx, int64_t groups, int64_t n, int64_t k,
+// Chunking of the selection: `chunks` workgroups of `chunk` rows per group, and
+// the workspace bytes it needs.
+struct SelectPlan {
+  int chunks;
+  int64_t chunk;
+  size_t ws_bytes;
+};
+SelectPlan select_plan(int64_t groups, int64_t n);
+hipError_t launch_select(const float* mass, int32_t* idx, void* ws, int64_t groups, int64_t n, int64_t k,
                          hipStream_t stream);
 int mass_max_rows();   // largest G * Bq the bf16 mass kernel supports
 int mass_tile_keys();  // keys per tile of the bf16 mass kernel

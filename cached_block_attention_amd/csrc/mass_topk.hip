@@ -33,6 +33,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2eM = 1.442695040888963407f;
 constexpr int kMassWaves = 8;
@@ -41,6 +42,22 @@ constexpr int kMassTile = 64;
 template <int CPR>
 __device__ __forceinline__ int mswz(int r) {
   return CPR == 16 ? (r & 15) : ((r ^ (r >> 3)) & 7);
+}
+
+// One halving step of the column sum over the 32 lanes of a wave half: lanes
+// whose bit M is set keep registers M..2M-1 (summed with the partner lane's),
+// the others registers 0..M-1; after the steps 16, 8, 4, 2, 1 lane n holds the
+// total of register n over the 32 lanes.
+template <int M>
+__device__ __forceinline__ void halve_sum(float* v, int n) {
+  const bool upper = (n & M) != 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const float send = upper ? v[i] : v[i + M];
+    const float keep = upper ? v[i + M] : v[i];
+    v[i] = keep + __shfl_xor(send, M);
+  }
+  if constexpr (M > 1) halve_sum<M / 2>(v, n);
 }
 
 // bf16: one workgroup of 8 waves per (key split, batch * kv head); wave w owns
@@ -101,23 +118,23 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
   // row 0 (their mass is never written)
   const char* kbase = (const char*)p.k + 2 * ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh);
   const int64_t kst = 2 * p.k_st;
-  uint4 stage[CPT];
-  auto load_tile = [&](int t) {
+  u32x4_t stage[CPT];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 64 * NW * i;
       const int row = c / CPR, ch = c - (c / CPR) * CPR;
       int64_t key = (int64_t)t * TK + row;
       key = key < p.n_keys ? key : 0;
-      stage[i] = *(const uint4*)(kbase + key * kst + 16 * ch);
+      stage[i] = *(const u32x4_t*)(kbase + key * kst + 16 * ch);
     }
   };
-  auto store_tile = [&](int slot) {
+  auto store_tile = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 64 * NW * i;
       const int row = c / CPR, ch = c - (c / CPR) * CPR;
-      *(uint4*)(kbuf[slot] + row * ROWB + 16 * (ch ^ mswz<CPR>(row))) = stage[i];
+      *(u32x4_t*)(kbuf[slot] + row * ROWB + 16 * (ch ^ mswz<CPR>(row))) = stage[i];
     }
   };
 
@@ -154,18 +171,9 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], c2, nl2[j]));
-      // sum over the 32 rows (lanes n of this half): halve the register count
-      // at every lane exchange; lane n keeps register n's column total
-#pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) {
-        const bool upper = (n & m) != 0;
-#pragma unroll
-        for (int i = 0; i < m; ++i) {
-          const float send = upper ? v[i] : v[i + m];
-          const float keep = upper ? v[i + m] : v[i];
-          v[i] = keep + __shfl_xor(send, m);
-        }
-      }
+      // sum over the 32 rows (lanes n of this half); lane n keeps register n's
+      // column total
+      halve_sum<16>(v, n);
       acc += v[0];
     }
     red[wave][kid] = acc;
@@ -208,112 +216,210 @@ __global__ __launch_bounds__(64) void mass_f32_kernel(const MassParams p) {
   p.mass[((int64_t)b * p.kv_heads + hkv) * p.n_keys + key] = acc;
 }
 
-// Selection of the n_keep largest masses of one (batch, kv head), ties to the
-// lower index, written in ascending index order.
-constexpr int kSelThreads = 1024;
+// Selection of the n_keep largest masses of each (batch, kv head), ties to the
+// lower index, written in ascending index order. Masses are finite and >= 0,
+// so their bit patterns (with -0 folded onto +0) order like the values. An
+// exact radix select finds the n_keep-th largest pattern T, 8 bits per pass from
+// the top; every pass spreads each group's row over `chunks` workgroups that
+// write per-chunk histograms, and each workgroup of the next pass sums those
+// histograms to find the digit itself. A count pass and an ordered write pass
+// then emit the rows above T and the lowest-indexed rows equal to T.
+//
+// Workspace (uint32): hist [4][G][C][256], counts [G][C][2], state [5][G][2]
+// with state[p] = (prefix of T fixed before pass p, rows still to take among
+// those matching it); state[4] = (T, ties taken).
+constexpr int kSelThreads = 256;
+constexpr int kSelMaxChunks = 32;
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* mass, int32_t* idx, int64_t n,
-                                                             int64_t k) {
-  __shared__ uint32_t hist[256];
-  __shared__ int64_t scan[kSelThreads];
-  __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_need;
+struct SelParams {
+  const uint32_t* bits;  // [G, n]
+  int32_t* idx;          // [G, k]
+  uint32_t* hist;
+  uint32_t* counts;
+  uint32_t* state;
+  int64_t n, k, chunk;
+  int groups, chunks;
+};
+
+__device__ __forceinline__ uint32_t sel_key(uint32_t x) { return x == 0x80000000u ? 0u : x; }
+
+// From the previous pass's state and its per-chunk histograms, the digit of T
+// at `shift` and the state after it. Every thread returns the same values.
+__device__ void sel_derive(const SelParams& p, int g, int pass_prev, uint32_t prev_prefix, uint32_t prev_need,
+                           uint32_t* s_bins, uint32_t* s_out, uint32_t& prefix, uint32_t& need) {
   const int tid = threadIdx.x;
-  const uint32_t* bits = (const uint32_t*)mass + (int64_t)blockIdx.x * n;
-  int32_t* out = idx + (int64_t)blockIdx.x * k;
-  if (k <= 0) return;
-  if (k >= n) {  // everything is kept
-    for (int64_t j = tid; j < n; j += kSelThreads) out[j] = (int32_t)j;
+  if (tid == 0) {  // kept only if the masses break the precondition
+    s_out[0] = prev_prefix;
+    s_out[1] = prev_need;
+  }
+  const uint32_t* h = p.hist + ((int64_t)pass_prev * p.groups + g) * p.chunks * 256;
+  uint32_t c = 0;
+  for (int ch = 0; ch < p.chunks; ++ch) c += h[ch * 256 + tid];
+  s_bins[tid] = c;
+  __syncthreads();
+  // inclusive suffix sums: s_bins[t] = rows whose digit is >= t
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t add = tid + off < 256 ? s_bins[tid + off] : 0u;
+    __syncthreads();
+    s_bins[tid] += add;
+    __syncthreads();
+  }
+  const uint32_t incl = s_bins[tid];
+  const uint32_t above = incl - c;
+  if (above < prev_need && prev_need <= incl) {
+    s_out[0] = prev_prefix | ((uint32_t)tid << (24 - 8 * pass_prev));
+    s_out[1] = prev_need - above;
+  }
+  __syncthreads();
+  prefix = s_out[0];
+  need = s_out[1];
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelParams p, int pass) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_bins[256];
+  __shared__ uint32_t s_out[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int c = blockIdx.x, g = blockIdx.y;
+  if (p.k >= p.n) return;
+  uint32_t prefix = 0, need = (uint32_t)p.k;
+  if (pass > 0) {
+    uint32_t pp = 0, pn = (uint32_t)p.k;
+    if (pass > 1) {
+      pp = p.state[((pass - 1) * p.groups + g) * 2];
+      pn = p.state[((pass - 1) * p.groups + g) * 2 + 1];
+    }
+    sel_derive(p, g, pass - 1, pp, pn, s_bins, s_out, prefix, need);
+    if (c == 0 && tid == 0) {
+      p.state[(pass * p.groups + g) * 2] = prefix;
+      p.state[(pass * p.groups + g) * 2 + 1] = need;
+    }
+  }
+  s_hist[tid] = 0;
+  __syncthreads();
+  const int shift = 24 - 8 * pass;
+  const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+  const uint32_t* row = p.bits + (int64_t)g * p.n;
+  const int64_t j0 = (int64_t)c * p.chunk;
+  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
+  for (int64_t j = j0 + tid; j - tid < j1; j += kSelThreads) {
+    const bool in = j < j1;
+    const uint32_t x = in ? sel_key(row[j]) : 0u;
+    const bool m = in && (x & hmask) == prefix;
+    const uint32_t dg = (x >> shift) & 255u;
+    // the wave's most common case (all rows in one bin) becomes a single atomic
+    const uint64_t act = __ballot(m);
+    if (act != 0) {
+      const int lead = __ffsll((unsigned long long)act) - 1;
+      const uint32_t d0 = __shfl(dg, lead);
+      const bool same = m && dg == d0;
+      const uint64_t smask = __ballot(same);
+      if (same) {
+        if (lane == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(smask));
+      } else if (m) {
+        atomicAdd(&s_hist[dg], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  p.hist[(((int64_t)pass * p.groups + g) * p.chunks + c) * 256 + tid] = s_hist[tid];
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelParams p) {
+  __shared__ uint32_t s_bins[256];
+  __shared__ uint32_t s_out[2];
+  __shared__ uint32_t s_red[2][kSelThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, g = blockIdx.y;
+  if (p.k >= p.n) return;
+  uint32_t T, ties;
+  sel_derive(p, g, 3, p.state[(3 * p.groups + g) * 2], p.state[(3 * p.groups + g) * 2 + 1], s_bins, s_out, T,
+             ties);
+  if (c == 0 && tid == 0) {
+    p.state[(4 * p.groups + g) * 2] = T;
+    p.state[(4 * p.groups + g) * 2 + 1] = ties;
+  }
+  const uint32_t* row = p.bits + (int64_t)g * p.n;
+  const int64_t j0 = (int64_t)c * p.chunk;
+  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
+  uint32_t gt = 0, eq = 0;
+  for (int64_t j = j0 + tid; j < j1; j += kSelThreads) {
+    const uint32_t x = sel_key(row[j]);
+    gt += x > T ? 1u : 0u;
+    eq += x == T ? 1u : 0u;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) {
+    s_red[0][wave] = gt;
+    s_red[1][wave] = eq;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    uint32_t t = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) t += s_red[tid][w];
+    p.counts[((int64_t)g * p.chunks + c) * 2 + tid] = t;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_write_kernel(SelParams p) {
+  constexpr int NW = kSelThreads / 64;
+  __shared__ uint32_t s_w[2][2][NW];  // [parity][gt, eq][wave]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x, g = blockIdx.y;
+  int32_t* out = p.idx + (int64_t)g * p.k;
+  const int64_t j0 = (int64_t)c * p.chunk;
+  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
+  if (p.k >= p.n) {  // every row is kept
+    for (int64_t j = j0 + tid; j < j1; j += kSelThreads) out[j] = (int32_t)j;
     return;
   }
-  // radix select of the k-th largest bit pattern, 8 bits per pass from the top
-  if (tid == 0) {
-    s_prefix = 0;
-    s_need = k;
+  const uint32_t T = p.state[(4 * p.groups + g) * 2];
+  const int64_t ties = p.state[(4 * p.groups + g) * 2 + 1];
+  int64_t gt_before = 0, eq_before = 0;
+  for (int ch = 0; ch < c; ++ch) {
+    gt_before += p.counts[((int64_t)g * p.chunks + ch) * 2];
+    eq_before += p.counts[((int64_t)g * p.chunks + ch) * 2 + 1];
   }
-  __syncthreads();
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    const uint32_t hmask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-    for (int64_t j = tid; j < n; j += kSelThreads) {
-      const uint32_t x = bits[j];
-      if ((x & hmask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t need = s_need, above = 0;
-      int dsel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (above + hist[dg] >= need) {
-          dsel = dg;
-          break;
-        }
-        above += hist[dg];
-      }
-      s_prefix = prefix | ((uint32_t)dsel << shift);
-      s_need = need - above;  // still to take among keys equal to the prefix so far
+  auto clamp_take = [](int64_t avail, int64_t cnt) -> int64_t {  // min(max(avail, 0), cnt)
+    return avail <= 0 ? 0 : (avail < cnt ? avail : cnt);
+  };
+  int64_t pos_run = gt_before + clamp_take(ties, eq_before);  // rows taken in earlier chunks
+  int64_t eq_run = eq_before;                                  // rank of the next row equal to T
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int it = 0;
+  for (int64_t jb = j0; jb < j1; jb += kSelThreads, ++it) {
+    const int64_t j = jb + tid;
+    const bool in = j < j1;
+    const uint32_t x = in ? sel_key(p.bits[(int64_t)g * p.n + j]) : 0u;
+    const bool gt = in && x > T;
+    const bool eq = in && x == T;
+    const uint64_t gm = __ballot(gt), em = __ballot(eq);
+    const int par = it & 1;
+    if (lane == 0) {
+      s_w[par][0][wave] = (uint32_t)__popcll(gm);
+      s_w[par][1][wave] = (uint32_t)__popcll(em);
     }
     __syncthreads();
-  }
-  const uint32_t T = s_prefix;
-  const int64_t ties_taken = s_need;  // keys equal to T that are kept: the lowest-indexed ones
-  // ordered compaction: contiguous chunks per thread, two block scans
-  const int64_t chunk = (n + kSelThreads - 1) / kSelThreads;
-  const int64_t j0 = (int64_t)tid * chunk;
-  const int64_t j1 = j0 + chunk < n ? j0 + chunk : n;
-  int64_t ties = 0;
-  for (int64_t j = j0; j < j1; ++j) ties += bits[j] == T ? 1 : 0;
-  scan[tid] = ties;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int i = 0; i < kSelThreads; ++i) {
-      const int64_t c = scan[i];
-      scan[i] = run;
-      run += c;
+    int64_t gt_pre = 0, eq_pre = 0, gt_tot = 0, eq_tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int64_t a = s_w[par][0][w], b = s_w[par][1][w];
+      if (w < wave) gt_pre += a, eq_pre += b;
+      gt_tot += a, eq_tot += b;
     }
-  }
-  __syncthreads();
-  const int64_t ties_before = scan[tid];
-  int64_t sel = 0;
-  {
-    int64_t tb = ties_before;
-    for (int64_t j = j0; j < j1; ++j) {
-      const uint32_t x = bits[j];
-      if (x > T) {
-        ++sel;
-      } else if (x == T) {
-        if (tb < ties_taken) ++sel;
-        ++tb;
-      }
+    const int64_t eq_base = eq_run + eq_pre;  // rank of this wave's first row equal to T
+    const int64_t eq_lane = __popcll(em & lt);
+    const bool take = gt || (eq && eq_base + eq_lane < ties);
+    if (take) {
+      const int64_t pos = pos_run + gt_pre + clamp_take(ties - eq_run, eq_pre) + __popcll(gm & lt) +
+                          clamp_take(ties - eq_base, eq_lane);
+      if (pos < p.k) out[pos] = (int32_t)j;
     }
-  }
-  __syncthreads();
-  scan[tid] = sel;
-  __syncthreads();
-  if (tid == 0) {
-    int64_t run = 0;
-    for (int i = 0; i < kSelThreads; ++i) {
-      const int64_t c = scan[i];
-      scan[i] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  int64_t pos = scan[tid];
-  int64_t tb = ties_before;
-  for (int64_t j = j0; j < j1; ++j) {
-    const uint32_t x = bits[j];
-    bool take = false;
-    if (x > T) {
-      take = true;
-    } else if (x == T) {
-      take = tb < ties_taken;
-      ++tb;
-    }
-    if (take && pos < k) out[pos++] = (int32_t)j;
+    pos_run += gt_tot + clamp_take(ties - eq_run, eq_tot);
+    eq_run += eq_tot;
   }
 }
 
@@ -354,10 +460,41 @@ hipError_t launch_mass(const MassParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_select(const float* mass, int32_t* idx, int64_t groups, int64_t n, int64_t k,
+SelectPlan select_plan(int64_t groups, int64_t n) {
+  SelectPlan sp{1, n > 0 ? n : 1, 0};
+  if (groups <= 0 || n <= 0) return sp;
+  int64_t c = (n + 1023) / 1024;                 // chunks of at least 1024 rows
+  const int64_t fill = (512 + groups - 1) / groups;  // about 256-512 workgroups in all
+  if (c > fill) c = fill;
+  if (c > kSelMaxChunks) c = kSelMaxChunks;
+  if (c < 1) c = 1;
+  int64_t chunk = (n + c - 1) / c;
+  chunk = (chunk + kSelThreads - 1) / kSelThreads * kSelThreads;
+  sp.chunk = chunk;
+  sp.chunks = (int)((n + chunk - 1) / chunk);
+  sp.ws_bytes = (size_t)(groups * sp.chunks * (4 * 256 + 2) + 5 * groups * 2) * sizeof(uint32_t);
+  return sp;
+}
+
+hipError_t launch_select(const float* mass, int32_t* idx, void* ws, int64_t groups, int64_t n, int64_t k,
                          hipStream_t stream) {
-  if (groups == 0 || k == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)groups), dim3(kSelThreads), 0, stream, mass, idx, n, k);
+  if (groups == 0 || k == 0 || n == 0) return hipSuccess;
+  const SelectPlan sp = select_plan(groups, n);
+  SelParams p;
+  p.bits = reinterpret_cast<const uint32_t*>(mass);
+  p.idx = idx;
+  p.hist = static_cast<uint32_t*>(ws);
+  p.counts = p.hist + groups * sp.chunks * 4 * 256;
+  p.state = p.counts + groups * sp.chunks * 2;
+  p.n = n, p.k = k, p.chunk = sp.chunk;
+  p.groups = (int)groups, p.chunks = sp.chunks;
+  const dim3 grid((unsigned)sp.chunks, (unsigned)groups);
+  if (k < n) {
+    for (int pass = 0; pass < 4; ++pass)
+      hipLaunchKernelGGL(select_hist_kernel, grid, dim3(kSelThreads), 0, stream, p, pass);
+    hipLaunchKernelGGL(select_count_kernel, grid, dim3(kSelThreads), 0, stream, p);
+  }
+  hipLaunchKernelGGL(select_write_kernel, grid, dim3(kSelThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ extern "C" {
 /* op codes for blkattn_workspace_bytes / blkattn_plan_splits */
 #define BLKATTN_OP_FULL 0
 #define BLKATTN_OP_PREFIX_PARTIAL 1
+#define BLKATTN_OP_SELECT 2 /* blkattn_select_retained */
 
 /* Problem sizes. */
 typedef struct blkattn_dims {
@@ -241,20 +242,28 @@ int blkattn_prefix_mass(const blkattn_dims* dims, const blkattn_tensor* q, const
  * blkattn_select_retained - per (batch, kv head), the n_keep prefix rows of
  * largest mass, ties broken towards the lower row, listed in ascending row
  * order: the index layout of blkattn_full / blkattn_gather_prefix.
- *   mass  fp32 [B, Hkv, prefix_len] contiguous, finite and >= 0
+ *   mass  fp32 [B, Hkv, prefix_len] contiguous, finite and >= 0 (-0 counts as 0)
  *   idx   int32 [B, Hkv, n_keep] contiguous output
- * Requires n_keep <= prefix_len. Deterministic (an exact radix selection).
+ *   workspace / workspace_bytes: device scratch of at least
+ *         blkattn_workspace_bytes(dims, BLKATTN_OP_SELECT) bytes, 16-byte
+ *         aligned; contents on entry are ignored. May be NULL when
+ *         n_keep == prefix_len (every row kept).
+ * Requires n_keep <= prefix_len <= INT32_MAX. Deterministic: an exact radix
+ * selection of the n_keep-th largest mass over several kernels on `stream`.
  */
-int blkattn_select_retained(const blkattn_dims* dims, const float* mass, int32_t* idx, void* stream);
+int blkattn_select_retained(const blkattn_dims* dims, const float* mass, int32_t* idx, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Workspace bytes blkattn_full / blkattn_prefix_partial need for these dims
- * (0 when the plan uses a single key split). The prefix is taken as indexed
+ * (0 when the plan uses a single key split), or blkattn_select_retained needs
+ * (op BLKATTN_OP_SELECT). The prefix is taken as indexed
  * with n_keep rows when n_keep > 0, else as prefix_len dense rows; an indexed
  * call with n_keep == 0 needs no more than this. Returns 0 for invalid dims. */
 size_t blkattn_workspace_bytes(const blkattn_dims* dims, int op);
 
-/* Number of key splits the plan uses for these dims and op (>= 1), or a
- * negative status for invalid dims. */
+/* Number of key splits the plan uses for these dims and op (>= 1; for
+ * BLKATTN_OP_SELECT the workgroups per (batch, kv head)), or a negative status
+ * for invalid dims. */
 int blkattn_plan_splits(const blkattn_dims* dims, int op);
 
 /*

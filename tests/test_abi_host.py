@@ -122,6 +122,24 @@ def test_split_plan_is_a_function_of_dims(lib):
     assert lib.blkattn_plan_splits(ctypes.byref(sparse), ba.OP_FULL) >= (100000 + 64) // 2048
 
 
+def test_select_plan_and_workspace(lib):
+    d = dims(batch=2, kv_heads=4, q_heads=4, n_keep=8192, prefix_len=131072, dtype=ba.F32)
+    chunks = lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_SELECT)
+    assert 1 <= chunks <= 32 and 8 * chunks >= 256          # the row is spread over the chip
+    need = lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_SELECT)
+    assert need >= 8 * chunks * 4 * 256 * 4                   # per-chunk histograms of four passes
+    small = dims(batch=1, kv_heads=1, q_heads=1, n_keep=3, prefix_len=100, dtype=ba.F32)
+    assert lib.blkattn_plan_splits(ctypes.byref(small), ba.OP_SELECT) == 1
+
+    def sel(dd, ws=None, nbytes=0):
+        return lib.blkattn_select_retained(ctypes.byref(dd), 4096, 8192, ws, nbytes, None)
+    assert sel(d) == ba.ERR_WORKSPACE
+    assert sel(d, 4096, need - 1) == ba.ERR_WORKSPACE
+    assert sel(d, 4104, need) == ba.ERR_MISALIGNED
+    assert sel(dims(n_keep=10, prefix_len=9)) == ba.ERR_INVALID_ARG
+    assert sel(dims(batch=0, n_keep=10)) == ba.OK
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 32, 64)

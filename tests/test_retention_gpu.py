@@ -89,6 +89,8 @@ def test_selection_ties_and_edges(ba):
     m = rng.integers(0, 40, size=(2, 3, P)).astype(np.float32)   # heavy ties
     m[1, 2] = 0.25                                                # all equal
     m[0, 1, ::2] = 1e-30                                          # tiny values
+    m[1, 0, 7::11] = -0.0                                         # -0 ranks as 0
+    m[1, 0, 3::13] = 0.0
     mt = torch.from_numpy(m).cuda()
     for k in (1, 2, 777, P - 1, P):
         idx = ba.select_retained(mt, k)
@@ -101,6 +103,27 @@ def test_selection_ties_and_edges(ba):
     idx = ba.select_retained(bt, 8192)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), oracle.select_retained(big.astype(np.float64), 8192))
+
+
+@pytest.mark.parametrize("groups,P,k", [(8, 131072, 8192), (3, 70001, 33333), (1, 1023, 500), (5, 300, 7)])
+def test_selection_ties_across_chunks(ba, groups, P, k):
+    """Rows equal to the k-th largest mass spread over every workgroup's chunk,
+    so the lower-index tie rule is decided across chunk boundaries; the rows
+    are not a multiple of the chunk or of a workgroup."""
+    import torch
+    rng = np.random.default_rng(groups * 1000 + k)
+    m = np.full((1, groups, P), 0.5, dtype=np.float32)
+    cols = rng.integers(0, P, size=P // 7)
+    m[0][:, cols] = rng.random(P // 7).astype(np.float32)[None, :]
+    m[0, 0, rng.integers(0, P, size=k // 3)] = 2.0                 # a set certainly above the ties
+    mt = torch.from_numpy(m).cuda()
+    dims = ba.Dims(1, groups, groups, 64, 1, k, P, ba.F32, 1.0, 0, 0)
+    ws = torch.empty(ba.workspace_bytes(dims, ba.OP_SELECT), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)                                                   # stale workspace contents are ignored
+    idx = torch.empty(1, groups, k, dtype=torch.int32, device="cuda")
+    ba.blkattn_select_retained(mt, idx, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.select_retained(m.astype(np.float64), k))
 
 
 def test_mass_is_deterministic(ba):

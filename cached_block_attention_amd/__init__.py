@@ -27,6 +27,7 @@ BF16 = 1
 OP_FULL = 0
 OP_PREFIX_PARTIAL = 1
 OP_SELECT = 2
+OP_SEQUENCE = 3
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -102,6 +103,8 @@ def library() -> ctypes.CDLL:
         "blkattn_merge": (ctypes.c_int, [pd, pp, pp, pt, vp, pp, vp]),
         "blkattn_gather_prefix": (ctypes.c_int, [pd, pt, pt, vp, pt, pt, vp]),
         "blkattn_prefix_mass": (ctypes.c_int, [pd, pt, pt, vp, vp, vp]),
+        "blkattn_sequence_step": (ctypes.c_int, [pd, ctypes.c_int64, ctypes.c_int, pt, pt, pt, pp, pt, vp, vp, sz,
+                                                 vp]),
         "blkattn_select_retained": (ctypes.c_int, [pd, vp, vp, vp, sz, vp]),
         "blkattn_workspace_bytes": (ctypes.c_size_t, [pd, ctypes.c_int]),
         "blkattn_plan_splits": (ctypes.c_int, [pd, ctypes.c_int]),
@@ -286,6 +289,25 @@ def blkattn_block_step(q, k_blk, v_blk, cached: Partial, o, lse=None, scale=None
     return o, lse
 
 
+def blkattn_sequence_step(q, k, v, block_start: int, block_len: int, cache: Partial, gen_step: bool, o,
+                          lse=None, scale=None, splits=0, workspace=None, stream=None):
+    """First-layer attention of the whole sequence (q [B, Hq, N, d], k/v
+    [B, Hkv, N, d]) at one step of the block at rows [block_start, +block_len),
+    with the FACache of the other rows' queries over the other rows' keys:
+    built when gen_step is true, reused otherwise. Writes o and lse [B, Hq, N]."""
+    _check_gpu(q, k, v, *cache, o, lse)
+    B, Hq, N, d = q.shape
+    dims = Dims(B, Hq, k.shape[1], d, int(block_len), 0, N, _dtype_code(q),
+                float(1.0 / math.sqrt(d) if scale is None else scale), splits, 0)
+    ws, nbytes = _workspace(dims, OP_SEQUENCE, q.device, workspace)
+    st = library().blkattn_sequence_step(ctypes.byref(dims), int(block_start), 1 if gen_step else 0,
+                                         _ref(_tensor(q)), _ref(_tensor(k)), _ref(_tensor(v)),
+                                         _ref(_partial(cache)), _ref(_tensor(o)), _ptr(lse), _ptr(ws), nbytes,
+                                         _stream(stream))
+    _raise(st)
+    return o, lse
+
+
 def blkattn_merge(a: Partial, b: Partial, o=None, lse=None, ab: Optional[Partial] = None,
                   dtype=None, stream=None):
     """Log-sum-exp merge of two partials; writes O (dtype of `o`), LSE and/or `ab`."""
@@ -393,6 +415,22 @@ def select_retained(mass, n_keep: int, workspace=None, stream=None):
     B, Hkv, _ = mass.shape
     idx = torch.empty(B, Hkv, n_keep, dtype=torch.int32, device=mass.device)
     return blkattn_select_retained(mass, idx, workspace=workspace, stream=stream)
+
+
+def sequence_step(q, k, v, block_start: int, block_len: int, cache: Optional[Partial] = None,
+                  gen_step: Optional[bool] = None, scale=None, stream=None):
+    """Allocate O, LSE (and the cache when none is given, which implies a first
+    step) and run blkattn_sequence_step; returns (o, lse, cache)."""
+    torch = _torch()
+    B, Hq, N, d = q.shape
+    if cache is None:
+        cache = empty_partial(B, Hq, N, d, q.device)
+        gen_step = True if gen_step is None else gen_step
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, dtype=torch.float32, device=q.device)
+    blkattn_sequence_step(q, k, v, block_start, block_len, cache, bool(gen_step), o, lse, scale=scale,
+                          stream=stream)
+    return o, lse, cache
 
 
 def gather_prefix(k_full, v_full, idx, stream=None):

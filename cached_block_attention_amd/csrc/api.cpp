@@ -182,6 +182,8 @@ void fill_keys(KeySeq& ks, const blkattn_dims* d, const blkattn_tensor* k_pre, c
   }
 }
 
+RowMap identity_rows(const blkattn_dims* d) { return RowMap{0, 0, d->block_len}; }
+
 AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Plan& pl) {
   AttnParams p{};
   p.batch = d->batch;
@@ -198,6 +200,7 @@ AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Pla
   p.tiles = pl.tiles;
   p.rows_per_wg = pl.rows_per_wg;
   p.row_chunks = pl.row_chunks;
+  p.rows = identity_rows(d);
   return p;
 }
 
@@ -210,6 +213,64 @@ int launch_attn(const blkattn_dims* d, const AttnParams& p, const Plan& pl, hipS
   return BLKATTN_OK;
 }
 
+int check_workspace(const WsLayout& wl, void* workspace, size_t workspace_bytes) {
+  if (wl.total == 0) return BLKATTN_OK;
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return BLKATTN_OK;
+}
+
+// The attention kernel over the plan's key splits, then (with several) the
+// fixed-order LSE merge of the split partials. Writes the final O (+ LSE)
+// when `o` is given, else the caller's partial `out`; both at p.rows's rows.
+int run_splits(const blkattn_dims* d, AttnParams& p, const Plan& pl, const blkattn_tensor* o, float* lse,
+               const blkattn_partial* out, void* workspace, hipStream_t s) {
+  int st;
+  if (pl.splits == 1) {
+    if (o != nullptr) {
+      p.out.mode = kOutFinal;
+      p.out.o = o->data;
+      p.out.o_sb = o->stride_b, p.out.o_sh = o->stride_h, p.out.o_st = o->stride_t;
+      p.out.lse = lse;
+    } else {
+      p.out.mode = kOutPartial;
+      p.out.po = out->o, p.out.pm = out->m, p.out.pl = out->l;
+    }
+    if ((st = launch_attn(d, p, pl, s))) return st;
+    return ok();
+  }
+  const WsLayout wl = ws_layout(d, pl.splits);
+  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
+  char* ws = (char*)workspace;
+  p.out.mode = kOutSplit;
+  p.out.po = (float*)(ws + wl.o);
+  p.out.pm = (float*)(ws + wl.m);
+  p.out.pl = (float*)(ws + wl.l);
+  p.out.split_rows = rows;
+  if ((st = launch_attn(d, p, pl, s))) return st;
+  MergeParams mp{};
+  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
+  mp.nsrc = pl.splits;
+  mp.strided = 1;
+  mp.split_rows = rows;
+  mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
+  mp.out_dtype = d->dtype;
+  mp.rows = p.rows;
+  if (o != nullptr) {
+    mp.o_final = o->data;
+    mp.o_sb = o->stride_b, mp.o_sh = o->stride_h, mp.o_st = o->stride_t;
+    mp.lse = lse;
+  } else {
+    mp.out_o = out->o, mp.out_m = out->m, mp.out_l = out->l;
+  }
+  hipError_t e = launch_merge(mp, s);
+  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int check_idx(const blkattn_dims* d, const int32_t* idx) {
   if (idx == nullptr) {
     if (d->n_keep != 0) return fail(BLKATTN_ERR_INVALID_ARG, "n_keep is set but idx is NULL");
@@ -220,6 +281,42 @@ int check_idx(const blkattn_dims* d, const int32_t* idx) {
   if (d->n_keep > 0 && d->prefix_len == 0)
     return fail(BLKATTN_ERR_INVALID_ARG, "n_keep > 0 with an empty prefix to index");
   return BLKATTN_OK;
+}
+
+// The three launches of a full-sequence step. The sequence has N = prefix_len
+// rows; the block C is rows [c0, c0 + Bq); U is the other N - Bq rows.
+struct SeqPlans {
+  blkattn_dims du;  // U queries (block_len = N - Bq)
+  blkattn_dims dc;  // C queries (block_len = Bq)
+  Plan cache;       // U queries over the U keys (first step of a block)
+  Plan cont;        // U queries over the C keys, from the cache (one split)
+  Plan block;       // C queries over all N keys
+  size_t ws = 0;
+};
+
+SeqPlans seq_plans(const blkattn_dims* d) {
+  SeqPlans sp;
+  const int64_t N = d->prefix_len;
+  sp.du = *d;
+  sp.du.block_len = (int32_t)(N - d->block_len);
+  sp.du.n_keep = 0;
+  sp.dc = *d;
+  sp.dc.n_keep = 0;
+  sp.cache = make_plan(&sp.du, N - d->block_len, false);
+  blkattn_dims du1 = sp.du;
+  du1.splits = 1;
+  sp.cont = make_plan(&du1, d->block_len, false);
+  sp.block = make_plan(&sp.dc, N, false);
+  const size_t a = ws_layout(&sp.du, sp.cache.splits).total;
+  const size_t b = ws_layout(&sp.dc, sp.block.splits).total;
+  sp.ws = a > b ? a : b;
+  return sp;
+}
+
+blkattn_tensor rows_from(const blkattn_tensor* t, int64_t row0, int eb) {
+  blkattn_tensor r = *t;
+  r.data = (char*)t->data + row0 * t->stride_t * eb;
+  return r;
 }
 
 }  // namespace
@@ -251,6 +348,11 @@ int blkattn_plan_splits(const blkattn_dims* d, int op) {
   int st = check_dims(d);
   if (st != BLKATTN_OK) return st;
   if (op == BLKATTN_OP_SELECT) return select_plan((int64_t)d->batch * d->kv_heads, d->prefix_len).chunks;
+  if (op == BLKATTN_OP_SEQUENCE) {
+    if (d->block_len > d->prefix_len) return fail(BLKATTN_ERR_INVALID_ARG, "block_len exceeds prefix_len");
+    if (d->prefix_len - d->block_len > INT32_MAX) return fail(BLKATTN_ERR_UNSUPPORTED, "sequence too long");
+    return seq_plans(d).block.splits;
+  }
   if (op != BLKATTN_OP_FULL && op != BLKATTN_OP_PREFIX_PARTIAL)
     return fail(BLKATTN_ERR_INVALID_ARG, "unknown op %d", op);
   const bool indexed = d->n_keep > 0;
@@ -263,6 +365,7 @@ size_t blkattn_workspace_bytes(const blkattn_dims* d, int op) {
   const int s = blkattn_plan_splits(d, op);
   if (s < 1) return 0;
   if (op == BLKATTN_OP_SELECT) return select_plan((int64_t)d->batch * d->kv_heads, d->prefix_len).ws_bytes;
+  if (op == BLKATTN_OP_SEQUENCE) return seq_plans(d).ws;
   return ws_layout(d, s).total;
 }
 
@@ -286,46 +389,10 @@ int blkattn_full(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_t
     return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
   const int64_t n_keys = n_pre + d->block_len;
   const Plan pl = make_plan(d, n_keys, idx != nullptr);
-  const WsLayout wl = ws_layout(d, pl.splits);
-  if (wl.total > 0) {
-    if (workspace == nullptr || workspace_bytes < wl.total)
-      return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
-                  workspace == nullptr ? (size_t)0 : workspace_bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-      return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  }
-  hipStream_t s = (hipStream_t)stream;
+  if ((st = check_workspace(ws_layout(d, pl.splits), workspace, workspace_bytes))) return st;
   AttnParams p = attn_params(d, q, pl);
   fill_keys(p.keys, d, k_pre, v_pre, idx, k_blk, v_blk, n_pre, d->block_len);
-  const int64_t rows = (int64_t)d->batch * d->q_heads * d->block_len;
-  if (pl.splits == 1) {
-    p.out.mode = kOutFinal;
-    p.out.o = o->data;
-    p.out.o_sb = o->stride_b, p.out.o_sh = o->stride_h, p.out.o_st = o->stride_t;
-    p.out.lse = lse;
-    if ((st = launch_attn(d, p, pl, s))) return st;
-    return ok();
-  }
-  char* ws = (char*)workspace;
-  p.out.mode = kOutPartial;
-  p.out.po = (float*)(ws + wl.o);
-  p.out.pm = (float*)(ws + wl.m);
-  p.out.pl = (float*)(ws + wl.l);
-  p.out.split_rows = rows;
-  if ((st = launch_attn(d, p, pl, s))) return st;
-  MergeParams mp{};
-  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
-  mp.nsrc = pl.splits;
-  mp.strided = 1;
-  mp.split_rows = rows;
-  mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
-  mp.out_dtype = d->dtype;
-  mp.o_final = o->data;
-  mp.o_sb = o->stride_b, mp.o_sh = o->stride_h, mp.o_st = o->stride_t;
-  mp.lse = lse;
-  hipError_t e = launch_merge(mp, s);
-  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return run_splits(d, p, pl, o, lse, nullptr, workspace, (hipStream_t)stream);
 }
 
 int blkattn_prefix_partial(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,
@@ -349,40 +416,10 @@ int blkattn_prefix_partial(const blkattn_dims* d, const blkattn_tensor* q, const
     return ok();
   }
   const Plan pl = make_plan(d, n_pre, idx != nullptr);
-  const WsLayout wl = ws_layout(d, pl.splits);
-  if (wl.total > 0) {
-    if (workspace == nullptr || workspace_bytes < wl.total)
-      return fail(BLKATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total,
-                  workspace == nullptr ? (size_t)0 : workspace_bytes);
-    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
-      return fail(BLKATTN_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-  }
+  if ((st = check_workspace(ws_layout(d, pl.splits), workspace, workspace_bytes))) return st;
   AttnParams p = attn_params(d, q, pl);
   fill_keys(p.keys, d, k_pre, v_pre, idx, nullptr, nullptr, n_pre, 0);
-  p.out.mode = kOutPartial;
-  if (pl.splits == 1) {
-    p.out.po = out->o, p.out.pm = out->m, p.out.pl = out->l;
-    p.out.split_rows = rows;
-    if ((st = launch_attn(d, p, pl, s))) return st;
-    return ok();
-  }
-  char* ws = (char*)workspace;
-  p.out.po = (float*)(ws + wl.o);
-  p.out.pm = (float*)(ws + wl.m);
-  p.out.pl = (float*)(ws + wl.l);
-  p.out.split_rows = rows;
-  if ((st = launch_attn(d, p, pl, s))) return st;
-  MergeParams mp{};
-  mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
-  mp.nsrc = pl.splits;
-  mp.strided = 1;
-  mp.split_rows = rows;
-  mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
-  mp.out_dtype = d->dtype;
-  mp.out_o = out->o, mp.out_m = out->m, mp.out_l = out->l;
-  hipError_t e = launch_merge(mp, s);
-  if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return run_splits(d, p, pl, nullptr, nullptr, out, workspace, s);
 }
 
 int blkattn_block_partial(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_blk,
@@ -461,6 +498,7 @@ int blkattn_merge(const blkattn_dims* d, const blkattn_partial* a, const blkattn
   if (o == nullptr && lse == nullptr && ab == nullptr) return ok();
   MergeParams mp{};
   mp.batch = d->batch, mp.q_heads = d->q_heads, mp.block_len = d->block_len, mp.head_dim = d->head_dim;
+  mp.rows = identity_rows(d);
   mp.nsrc = 2;
   mp.strided = 0;
   mp.src_o[0] = a->o, mp.src_m[0] = a->m, mp.src_l[0] = a->l;
@@ -475,6 +513,62 @@ int blkattn_merge(const blkattn_dims* d, const blkattn_partial* a, const blkattn
   hipError_t e = launch_merge(mp, (hipStream_t)stream);
   if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int blkattn_sequence_step(const blkattn_dims* d, int64_t block_start, int gen_step, const blkattn_tensor* q,
+                          const blkattn_tensor* k, const blkattn_tensor* v, const blkattn_partial* cache,
+                          const blkattn_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  const int64_t N = d->prefix_len;
+  const int64_t Bq = d->block_len;
+  if (d->n_keep != 0) return fail(BLKATTN_ERR_INVALID_ARG, "n_keep must be 0 for a sequence step");
+  if (d->batch == 0 || d->q_heads == 0 || N == 0) return ok();
+  if (Bq == 0) return fail(BLKATTN_ERR_INVALID_ARG, "a sequence step needs a block (block_len > 0)");
+  if (block_start < 0 || block_start > N - Bq)
+    return fail(BLKATTN_ERR_INVALID_ARG, "block rows [%lld, %lld) do not lie in the %lld sequence rows",
+                (long long)block_start, (long long)(block_start + Bq), (long long)N);
+  if (N - Bq > INT32_MAX) return fail(BLKATTN_ERR_UNSUPPORTED, "sequence too long");
+  const int eb = elt_bytes(d->dtype);
+  const int64_t nu = N - Bq;
+  if ((st = check_tensor(q, "q", eb, 1))) return st;
+  if ((st = check_tensor(k, "k", eb, 1))) return st;
+  if ((st = check_tensor(v, "v", eb, 1))) return st;
+  if ((st = check_tensor(o, "o", eb, 1))) return st;
+  if ((st = check_partial(cache, "cache", nu))) return st;
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  const SeqPlans sp = seq_plans(d);
+  if (sp.ws > 0 && (st = check_workspace(WsLayout{0, 0, 0, sp.ws}, workspace, workspace_bytes))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const RowMap rows_u{block_start, Bq, N};  // U queries skip the block's rows
+  const RowMap rows_c{0, block_start, N};   // C queries start at the block's first row
+  if (nu > 0) {
+    if (gen_step) {
+      // first step of the block: the cache is the U queries' state over the U keys
+      AttnParams p = attn_params(&sp.du, q, sp.cache);
+      p.rows = rows_u;
+      fill_keys(p.keys, &sp.du, k, v, nullptr, nullptr, nullptr, nu, 0);
+      p.keys.p_rows = N;
+      p.keys.k_hole = block_start, p.keys.k_hole_len = Bq;
+      if ((st = run_splits(&sp.du, p, sp.cache, nullptr, nullptr, cache, workspace, s))) return st;
+    }
+    // U queries: start from the cache and attend the block's keys only
+    const blkattn_tensor kc = rows_from(k, block_start, eb), vc = rows_from(v, block_start, eb);
+    blkattn_dims du1 = sp.du;
+    du1.splits = 1;
+    AttnParams p = attn_params(&du1, q, sp.cont);
+    p.rows = rows_u;
+    fill_keys(p.keys, &du1, nullptr, nullptr, nullptr, &kc, &vc, 0, (int32_t)Bq);
+    p.init_o = cache->o, p.init_m = cache->m, p.init_l = cache->l;
+    if ((st = run_splits(&du1, p, sp.cont, o, lse, nullptr, nullptr, s))) return st;
+  }
+  // C queries: every key of the sequence
+  AttnParams p = attn_params(&sp.dc, q, sp.block);
+  p.rows = rows_c;
+  fill_keys(p.keys, &sp.dc, k, v, nullptr, nullptr, nullptr, N, 0);
+  return run_splits(&sp.dc, p, sp.block, o, lse, nullptr, workspace, s);
 }
 
 int blkattn_prefix_mass(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,

@@ -190,9 +190,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
     qi = prow - g * p.block_len;
   }
   const int hq = hkv * p.group + g;
+  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);  // sequence row
+  const int64_t mrow = ((int64_t)b * p.q_heads + hq) * p.rows.row_pitch + srow;  // per-row arrays
   bf16x8_t qf[D / 16];
   {
-    const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + hq * p.q_sh + qi * p.q_st;
+    const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + hq * p.q_sh + srow * p.q_st;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -221,10 +223,12 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
       const char* base = isv ? vpre : kpre;
       int64_t st = isv ? vp_st : kp_st;
       int64_t row = key0 + r;
-      if (!dense) {
+      if (dense) {
+        row += row >= p.keys.k_hole ? p.keys.k_hole_len : 0;
+      } else {
         int64_t key = row < n_all ? row : n_all - 1;  // rows past the end: any valid row (weight 0)
         if (key < n_pre) {
-          row = indexed ? (int64_t)sidx[key - kbeg] : key;
+          row = indexed ? (int64_t)sidx[key - kbeg] : key + (key >= p.keys.k_hole ? p.keys.k_hole_len : 0);
         } else {
           row = key - n_pre;
           base = isv ? vblk : kblk;
@@ -259,15 +263,14 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   // (m, l, O~) of a later step starts from the cache): O~ = l * o, m in base 2,
   // l carried by the lanes of the first wave half.
   if (p.init_m != nullptr && row_ok) {
-    const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
-    const float mi = p.init_m[prow_flat];
-    const float li = p.init_l[prow_flat];
+    const float mi = p.init_m[mrow];
+    const float li = p.init_l[mrow];
     if (mi > -INFINITY && li > 0.0f) {
       m2 = mi * kLog2e;
       mtrue = m2;
       lsum = h == 0 ? li : 0.0f;
       lhat = lsum;
-      const float* orow = p.init_o + prow_flat * D;
+      const float* orow = p.init_o + mrow * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -397,9 +400,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   const bool live = ltot > 0.0f;
   const float inv = live ? 1.0f / lhtot : 0.0f;
   if (!row_ok) return;
-  const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
   if (p.out.mode == kOutFinal) {
-    uint16_t* orow = (uint16_t*)p.out.o + b * p.out.o_sb + hq * p.out.o_sh + qi * p.out.o_st;
+    uint16_t* orow = (uint16_t*)p.out.o + b * p.out.o_sb + hq * p.out.o_sh + srow * p.out.o_st;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -415,9 +417,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
         *(uint2*)(orow + d0) = w;
       }
     if (p.out.lse != nullptr && h == 0)
-      p.out.lse[prow_flat] = live ? (m2 + __log2f(ltot)) * kLn2 : -INFINITY;
+      p.out.lse[mrow] = live ? (m2 + __log2f(ltot)) * kLn2 : -INFINITY;
   } else {
-    const int64_t base = (int64_t)split * p.out.split_rows + prow_flat;
+    const int64_t base = p.out.mode == kOutSplit
+                             ? (int64_t)split * p.out.split_rows + ((int64_t)b * p.q_heads + hq) * p.block_len + qi
+                             : mrow;
     float* orow = p.out.po + base * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

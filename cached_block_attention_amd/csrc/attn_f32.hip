@@ -20,7 +20,7 @@ constexpr int kF32Tile = 32;
 __device__ __forceinline__ const float* key_row_f32(const KeySeq& ks, int b, int hkv, int kv_heads,
                                                     int64_t j, bool want_v) {
   if (j < ks.n_pre) {
-    int64_t row = j;
+    int64_t row = j + (j >= ks.k_hole ? ks.k_hole_len : 0);
     if (ks.idx != nullptr) {
       int64_t r = ks.idx[((int64_t)b * kv_heads + hkv) * ks.n_pre + j];
       row = r < 0 ? 0 : (r >= ks.p_rows ? ks.p_rows - 1 : r);
@@ -52,7 +52,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     const bool ok = qi < p.block_len;
     float q[D];
     float o[D];
-    const float* qrow = (const float*)p.q + b * p.q_sb + hq * p.q_sh + (int64_t)(ok ? qi : 0) * p.q_st;
+    const int64_t srow = ok ? qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0) : 0;  // sequence row
+    const int64_t mrow = ((int64_t)b * p.q_heads + hq) * p.rows.row_pitch + srow;      // per-row arrays
+    const float* qrow = (const float*)p.q + b * p.q_sb + hq * p.q_sh + srow * p.q_st;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       q[d] = ok ? qrow[d] : 0.0f;
@@ -61,14 +63,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     float m = -INFINITY, l = 0.0f;
     if (p.init_m != nullptr && ok) {
       // initial state from a cached partial: O~ = l * o (LaCache Appendix J)
-      const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
-      const float mi = p.init_m[prow_flat];
-      const float li = p.init_l[prow_flat];
+      const float mi = p.init_m[mrow];
+      const float li = p.init_l[mrow];
       if (mi > -INFINITY && li > 0.0f) {
         m = mi;
         l = li;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = p.init_o[prow_flat * D + d] * li;
+        for (int d = 0; d < D; ++d) o[d] = p.init_o[mrow * D + d] * li;
       }
     }
     for (int t = t0; t < t1; ++t) {
@@ -114,15 +115,16 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     if (!ok) continue;
     const bool live = l > 0.0f;
     const float inv = live ? 1.0f / l : 0.0f;
-    const int64_t prow_flat = ((int64_t)b * p.q_heads + hq) * p.block_len + qi;
     if (p.out.mode == kOutFinal) {
-      float* orow = (float*)p.out.o + b * p.out.o_sb + hq * p.out.o_sh + qi * p.out.o_st;
+      float* orow = (float*)p.out.o + b * p.out.o_sb + hq * p.out.o_sh + srow * p.out.o_st;
 #pragma unroll
       for (int d = 0; d < D; d += 4)
         *(float4*)(orow + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-      if (p.out.lse != nullptr) p.out.lse[prow_flat] = live ? m + logf(l) : -INFINITY;
+      if (p.out.lse != nullptr) p.out.lse[mrow] = live ? m + logf(l) : -INFINITY;
     } else {
-      const int64_t base = (int64_t)split * p.out.split_rows + prow_flat;
+      const int64_t base = p.out.mode == kOutSplit
+                               ? (int64_t)split * p.out.split_rows + ((int64_t)b * p.q_heads + hq) * p.block_len + qi
+                               : mrow;
       float* orow = p.out.po + base * D;
 #pragma unroll
       for (int d = 0; d < D; d += 4)

@@ -20,6 +20,9 @@ struct KeySeq {
   const int32_t* idx;           // [B, Hkv, n_pre] or nullptr
   int64_t p_rows;               // rows of k_pre/v_pre (clamp bound for idx)
   int64_t n_pre;                // prefix keys attended (P, or n_keep with idx)
+  // Dense prefix key j reads row j + (j >= k_hole ? k_hole_len : 0): a prefix
+  // that skips the rows of a block sitting inside the sequence.
+  int64_t k_hole, k_hole_len;
   const void* k_blk;
   const void* v_blk;
   int64_t kb_sb, kb_sh, kb_st;
@@ -29,8 +32,9 @@ struct KeySeq {
 
 // Where a partial-attention launch writes.
 enum OutMode : int32_t {
-  kOutFinal = 0,    // O in the input dtype (strided) + optional LSE
-  kOutPartial = 1,  // contiguous fp32 partial (o, m, l); split s at offset s*split rows
+  kOutFinal = 0,    // O in the input dtype (strided) + optional LSE, at mapped rows
+  kOutPartial = 1,  // the caller's fp32 partial (o, m, l), at mapped rows
+  kOutSplit = 2,    // workspace partials, packed rows; split s at offset s * split_rows
 };
 
 struct OutDesc {
@@ -41,7 +45,16 @@ struct OutDesc {
   float* po;                    // partial o base
   float* pm;                    // partial m base
   float* pl;                    // partial l base
-  int64_t split_rows;           // rows of one split's partial (B*Hq*Bq) when split
+  int64_t split_rows;           // rows of one split's partial (B*Hq*Bq) in kOutSplit
+};
+
+// Query-row map. Packed row qi of a head reads sequence row
+// qi + (qi >= q_hole ? q_hole_len : 0) of q and of the final O; the per-row
+// arrays outside the split workspace (LSE, a caller's partial, the initial
+// state) hold that row at ((b * Hq + hq) * row_pitch + sequence row). With
+// q_hole_len == 0 and row_pitch == block_len this is the identity.
+struct RowMap {
+  int64_t q_hole, q_hole_len, row_pitch;
 };
 
 struct AttnParams {
@@ -56,6 +69,7 @@ struct AttnParams {
   int32_t tiles;        // ceil((n_pre + n_blk) / tile keys of this kernel)
   int32_t rows_per_wg;  // packed (q-head, query) rows one workgroup owns
   int32_t row_chunks;   // workgroups along the packed rows of one kv-head
+  RowMap rows;
   // Optional initial state (one key split only): contiguous fp32 partial
   // (o [rows, d], m, l [rows]) the running state starts from instead of the
   // empty state; nullptr when absent.
@@ -80,6 +94,8 @@ struct MergeParams {
   float* out_o;               // merged partial or nullptr
   float* out_m;
   float* out_l;
+  RowMap rows;                // outputs and explicit sources at mapped rows;
+                              // strided (workspace) sources at packed rows
 };
 
 struct GatherParams {

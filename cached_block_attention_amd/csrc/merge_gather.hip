@@ -33,6 +33,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
+  const int64_t hb = row / p.block_len;  // b * Hq + hq
+  const int64_t qi = row - hb * p.block_len;
+  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);  // sequence row
+  const int64_t mrow = hb * p.rows.row_pitch + srow;                      // per-row arrays
 
   float M = -INFINITY;
   float L = 0.0f;
@@ -55,9 +59,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
           po = p.src_o[0] + e * D;
         } else {
           const int si = s < 2 ? s : 1;  // two explicit sources
-          ms[i] = p.src_m[si][row];
-          ls[i] = p.src_l[si][row];
-          po = p.src_o[si] + row * D;
+          ms[i] = p.src_m[si][mrow];
+          ls[i] = p.src_l[si][mrow];
+          po = p.src_o[si] + mrow * D;
         }
         os[i] = *(const float4*)(po + 4 * c4);
       }
@@ -88,10 +92,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const float mo = live ? M : -INFINITY;
 
   if (p.o_final != nullptr) {
-    const int64_t hb = row / p.block_len;       // b * Hq + hq
-    const int64_t qi = row - hb * p.block_len;
     const int64_t b = hb / p.q_heads, hq = hb - (hb / p.q_heads) * p.q_heads;
-    const int64_t off = b * p.o_sb + hq * p.o_sh + qi * p.o_st + 4 * c4;
+    const int64_t off = b * p.o_sb + hq * p.o_sh + srow * p.o_st + 4 * c4;
     if (p.out_dtype == 0) {
       *(float4*)((float*)p.o_final + off) = o;
     } else {
@@ -102,12 +104,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       *(uint2*)((uint16_t*)p.o_final + off) = w;
     }
   }
-  if (p.lse != nullptr && c4 == 0) p.lse[row] = live ? M + logf(L) : -INFINITY;
+  if (p.lse != nullptr && c4 == 0) p.lse[mrow] = live ? M + logf(L) : -INFINITY;
   if (p.out_o != nullptr) {
-    *(float4*)(p.out_o + row * D + 4 * c4) = o;
+    *(float4*)(p.out_o + mrow * D + 4 * c4) = o;
     if (c4 == 0) {
-      p.out_m[row] = mo;
-      p.out_l[row] = live ? L : 0.0f;
+      p.out_m[mrow] = mo;
+      p.out_l[mrow] = live ? L : 0.0f;
     }
   }
 }

@@ -14,14 +14,20 @@ Workloads (the five shapes the method is exercised on):
   reuse_bf16   bf16, B8, H32/32, d128, P16384, Bq32, 8 denoising steps
   sparse_gqa   bf16, B2, Hq28/Hkv4, d128, P_full 131072, n_keep 8192, Bq64,
                per-(batch, kv-head) sorted distinct int32 row indices
+  llada_seq    bf16, B1, H32/32, d128, a 4096-row sequence whose block is rows
+               [2048, 2080), 8 denoising steps (full-sequence FACache step:
+               prompt and earlier blocks before the block, masked suffix after)
 
 Generator: numpy PCG64 ``standard_normal`` in float32, rounded to bfloat16 with
 round-to-nearest-even (kept as uint16 bit patterns; numpy has no bf16 type) or
 kept as float32 for the fp32 workload. Layout [B, H, rows, d], contiguous.
 
-Seeds: workload c (1..5) uses base 1000*c; streams base+1 Q, +2 K_prefix,
+Seeds: workload c (1..6) uses base 1000*c; streams base+1 Q, +2 K_prefix,
 +3 V_prefix, +4 K_block, +5 V_block, +6 outlier rows, +7 indices. Denoising
 step t of the reuse workload draws Q_t, K_t, V_t from base + 100*(t+1) + {1,4,5}.
+The sequence workload draws the whole sequence's Q, K, V from base + {1, 2, 3};
+at step t >= 1 the block rows of each are redrawn from base + 100*(t+1) + {1, 2, 3}
+and every other row keeps its value (LaCache: U token ids do not change).
 """
 
 from __future__ import annotations
@@ -93,6 +99,7 @@ class Shape:
     outlier_scale: float = 4.0
     steps: int = 1
     seed_base: int = 0
+    block_start: Optional[int] = None  # sequence workloads: the block's first row
 
     @property
     def group(self) -> int:
@@ -121,6 +128,9 @@ WORKLOADS = {
                         seed_base=4000),
     "sparse_gqa": Shape("sparse_gqa", BF16, 2, 28, 4, 128, 131072, 64, n_keep=8192,
                         seed_base=5000),
+    # prefix_len is the sequence length N here; the block is rows [block_start, +block_len)
+    "llada_seq": Shape("llada_seq", BF16, 1, 32, 32, 128, 4096, 32, steps=8, seed_base=6000,
+                       block_start=2048),
 }
 
 
@@ -196,3 +206,22 @@ def step_inputs(shape: Shape, t: int, seed_base: Optional[int] = None):
 def scaled_shape(name: str, **overrides) -> Shape:
     """A workload with some sizes overridden (small parity cases)."""
     return dataclasses.replace(WORKLOADS[name], **overrides)
+
+
+def sequence_inputs(shape: Shape, t: int = 0, seed_base: Optional[int] = None):
+    """(q [B, Hq, N, d], k, v [B, Hkv, N, d]) of the whole sequence at denoising
+    step t: step 0 draws every row; a later step redraws only the block's rows
+    (rows [block_start, block_start + block_len)), the others keep step 0's values."""
+    base = shape.seed_base if seed_base is None else seed_base
+    B, Hq, Hkv, d, N, dt = (shape.batch, shape.q_heads, shape.kv_heads, shape.head_dim,
+                            shape.prefix_len, shape.dtype)
+    c0, Bq = shape.block_start, shape.block_len
+    q = _normal(base + 1, (B, Hq, N, d), dt)
+    k = _normal(base + 2, (B, Hkv, N, d), dt)
+    v = _normal(base + 3, (B, Hkv, N, d), dt)
+    if t > 0:
+        sb = base + 100 * (t + 1)
+        q[:, :, c0:c0 + Bq] = _normal(sb + 1, (B, Hq, Bq, d), dt)
+        k[:, :, c0:c0 + Bq] = _normal(sb + 2, (B, Hkv, Bq, d), dt)
+        v[:, :, c0:c0 + Bq] = _normal(sb + 3, (B, Hkv, Bq, d), dt)
+    return q, k, v

@@ -82,6 +82,7 @@ extern "C" {
 #define BLKATTN_OP_FULL 0
 #define BLKATTN_OP_PREFIX_PARTIAL 1
 #define BLKATTN_OP_SELECT 2 /* blkattn_select_retained */
+#define BLKATTN_OP_SEQUENCE 3 /* blkattn_sequence_step */
 
 /* Problem sizes. */
 typedef struct blkattn_dims {
@@ -220,6 +221,39 @@ int blkattn_gather_prefix(const blkattn_dims* dims, const blkattn_tensor* k_full
                           const blkattn_tensor* k_out, const blkattn_tensor* v_out, void* stream);
 
 /*
+ * blkattn_sequence_step - first-layer attention of every token of the sequence
+ * at one denoising step of a block, with FACache (LaCache section 3.3.3 and
+ * the Appendix J pseudocode of its first-layer FlashAttention). The block C is
+ * the rows [block_start, block_start + block_len) of the N = prefix_len
+ * sequence rows; U is every other row (prompt, earlier blocks and the masked
+ * suffix), whose q, k and v stay fixed while the block is denoised.
+ *   gen_step != 0 (the block's first step): cache <- the partial state of the
+ *     U queries over the U keys (section 3.3.3: the tiles with both queries and
+ *     keys in U). Then, at every step:
+ *   U queries: the running state starts from the cache and continues over the
+ *     block's keys only (the tiles overlapping C), giving their O and LSE;
+ *   C queries: attention over all N keys.
+ * The result is plain attention over the whole sequence as long as the U rows
+ * are the ones the cache was built from (the cache is exact, not approximate).
+ *   q      [B, Hq, N, d];  k, v [B, Hkv, N, d]
+ *   cache  contiguous fp32 partial over the sequence rows: o [B, Hq, N, d],
+ *          m, l [B, Hq, N]. Written when gen_step != 0, read otherwise; its
+ *          block rows are neither read nor written. Same layout and meaning as
+ *          blkattn_partial elsewhere (o normalised, m in natural-log units).
+ *   o      [B, Hq, N, d] output, dtype of q;  lse fp32 [B, Hq, N] or NULL
+ *   workspace / workspace_bytes: blkattn_workspace_bytes(dims,
+ *          BLKATTN_OP_SEQUENCE) bytes, 16-byte aligned (NULL when 0).
+ * dims: prefix_len = N, block_len = the block's rows (>= 1), n_keep = 0;
+ * splits applies to the launches over many keys. Up to three kernels (four with
+ * split merges) are enqueued on `stream` in order; o, lse and cache must not
+ * alias q, k or v.
+ */
+int blkattn_sequence_step(const blkattn_dims* dims, int64_t block_start, int gen_step, const blkattn_tensor* q,
+                          const blkattn_tensor* k, const blkattn_tensor* v, const blkattn_partial* cache,
+                          const blkattn_tensor* o, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * blkattn_prefix_mass - attention mass of every dense prefix row:
  *   mass[b, h, j] = sum over the q-heads g of kv head h and the block queries i
  *                   of exp(scale * <q[b, g, i], k_pre[b, h, j]> - lse[b, g, i])
@@ -255,8 +289,8 @@ int blkattn_select_retained(const blkattn_dims* dims, const float* mass, int32_t
                             size_t workspace_bytes, void* stream);
 
 /* Workspace bytes blkattn_full / blkattn_prefix_partial need for these dims
- * (0 when the plan uses a single key split), or blkattn_select_retained needs
- * (op BLKATTN_OP_SELECT). The prefix is taken as indexed
+ * (0 when the plan uses a single key split), or blkattn_select_retained
+ * (op BLKATTN_OP_SELECT) or blkattn_sequence_step (op BLKATTN_OP_SEQUENCE) need. The prefix is taken as indexed
  * with n_keep rows when n_keep > 0, else as prefix_len dense rows; an indexed
  * call with n_keep == 0 needs no more than this. Returns 0 for invalid dims. */
 size_t blkattn_workspace_bytes(const blkattn_dims* dims, int op);

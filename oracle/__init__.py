@@ -18,3 +18,4 @@ from .attention import (  # noqa: F401
     state_from_partial,
 )
 from .retention import prefix_mass, select_retained  # noqa: F401
+from .sequence import sequence_full, facache_step, split_rows  # noqa: F401

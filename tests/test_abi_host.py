@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = header_symbols()
-    assert len(syms) == 14, syms
+    assert len(syms) == 15, syms
     for s in syms:
         assert hasattr(lib, s), s
 
@@ -138,6 +138,30 @@ def test_select_plan_and_workspace(lib):
     assert sel(d, 4104, need) == ba.ERR_MISALIGNED
     assert sel(dims(n_keep=10, prefix_len=9)) == ba.ERR_INVALID_ARG
     assert sel(dims(batch=0, n_keep=10)) == ba.OK
+
+
+def test_sequence_step_rejects_before_launch(lib):
+    d = dims(q_heads=4, kv_heads=4, prefix_len=1000, block_len=32)
+    t = ba.Tensor(4096, 128 * 1000, 128 * 1000, 128)
+    cache = ba.PartialDesc(8192, 4096, 4096)
+
+    def call(c0, dd=d, gen=1, c=cache, ws=None, nbytes=0):
+        return lib.blkattn_sequence_step(ctypes.byref(dd), c0, gen, ctypes.byref(t), ctypes.byref(t),
+                                         ctypes.byref(t), None if c is None else ctypes.byref(c), ctypes.byref(t),
+                                         None, ws, nbytes, None)
+    assert call(-1) == ba.ERR_INVALID_ARG
+    assert call(1000 - 31) == ba.ERR_INVALID_ARG                 # block past the end
+    assert call(0, dd=dims(q_heads=4, kv_heads=4, prefix_len=1000, block_len=0)) == ba.ERR_INVALID_ARG
+    assert call(0, dd=dims(q_heads=4, kv_heads=4, prefix_len=1000, n_keep=5)) == ba.ERR_INVALID_ARG
+    assert call(0, c=None) == ba.ERR_INVALID_ARG                 # rows outside the block need a cache
+    assert call(0, c=ba.PartialDesc(8200, 4096, 4096)) == ba.ERR_MISALIGNED
+    need = lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_SEQUENCE)
+    if need:
+        assert call(500) == ba.ERR_WORKSPACE
+    assert call(0, dd=dims(batch=0, prefix_len=1000)) == ba.OK    # empty batch: no-op
+    # the plan: the block's queries over all 1000 keys fill the chip with key splits
+    assert lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_SEQUENCE) >= 1
+    assert lib.blkattn_plan_splits(ctypes.byref(dims(prefix_len=10, block_len=32)), ba.OP_SEQUENCE) < 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -14,6 +14,7 @@ HIP events around that kernel on its stream), and the fp64 CPU oracle timed on
 the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--path full|cached]
+  python bench.py --extra          # also one JSON line per secondary path
   python bench.py --copy-probe     # plain device copy of known size (counter scale)
 """
 
@@ -243,13 +244,48 @@ def extra_lines(reps: int):
         del t, pbq
         torch.cuda.empty_cache()
 
+    # full-sequence FACache step (LLaDA-like: 4096 rows, block at rows 2048..2079):
+    # the block's first step builds the cache, later steps reuse it; against
+    # plain attention of every row over every row at each step
+    sh = datagen.WORKLOADS["llada_seq"]
+    B, Hq, N, d, Bq, c0 = sh.batch, sh.q_heads, sh.prefix_len, sh.head_dim, sh.block_len, sh.block_start
+    q, k, v = (up(x, torch) for x in datagen.sequence_inputs(sh, 0))
+    cache = ba.empty_partial(B, Hq, N, d, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
+    dims = ba.Dims(B, Hq, sh.kv_heads, d, Bq, 0, N, ba.BF16, float(sh.scale), 0, 0)
+    ws = torch.empty(max(1, ba.workspace_bytes(dims, ba.OP_SEQUENCE)), dtype=torch.uint8, device="cuda")
+    ms_gen = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, True, o, lse, workspace=ws), reps)
+    ms_step = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, False, o, lse, workspace=ws), reps)
+    full = ba.empty_partial(B, Hq, N, d, "cuda")
+    ms_full = _median_ms(lambda: ba.blkattn_prefix_partial(q, k, v, full), reps)
+    nu = N - Bq
+    fl_gen = 4.0 * B * Hq * (nu * nu + nu * Bq + Bq * N) * d
+    fl_step = 4.0 * B * Hq * (nu * Bq + Bq * N) * d
+    fl_full = 4.0 * B * Hq * N * N * d
+    # a reuse step reads q, the cached (o, m, l) of the other rows and the whole
+    # sequence's k, v (for the block queries), and writes o and lse
+    step_bytes = (2.0 * B * Hq * N * d + 4.0 * B * Hq * nu * (d + 2) + 2 * 2.0 * B * sh.kv_heads * N * d
+                  + 2.0 * B * Hq * N * d + 4.0 * B * Hq * N)
+    n = sh.steps
+    amort = (ms_gen + (n - 1) * ms_step) / n
+    emit(path="blkattn_sequence_step", workload=f"llada_seq B1 H32 d128 N{N} block [{c0},{c0 + Bq}), {n} steps",
+         first_step_ms=round(ms_gen, 4), first_step_tflops=round(fl_gen / ms_gen / 1e9, 1),
+         reuse_step_ms=round(ms_step, 4), reuse_step_tflops=round(fl_step / ms_step / 1e9, 1),
+         reuse_step_hbm_gbps=round(step_bytes / ms_step / 1e6, 1),
+         full_attention_ms=round(ms_full, 4), full_attention_tflops=round(fl_full / ms_full / 1e9, 1),
+         amortized_ms_per_step=round(amort, 4), facache_gain=round(ms_full / amort, 2))
+    del q, k, v, cache, o, lse, ws, full
+    torch.cuda.empty_cache()
+
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dream_gqa", choices=sorted(datagen.WORKLOADS))
+    ap.add_argument("--workload", default="dream_gqa",
+                    choices=sorted(k for k, w in datagen.WORKLOADS.items() if w.block_start is None))
     ap.add_argument("--path", default="full", choices=["full", "cached"],
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")

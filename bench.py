@@ -133,10 +133,14 @@ def _median_ms(fn, reps: int, warm: int = 3):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
-def extra_lines(reps: int):
+EXTRA_PATHS = ("prefix", "llada", "reuse", "retention", "large", "sequence")
+
+
+def extra_lines(reps: int, paths=EXTRA_PATHS):
     """Timings of the other paths (one JSON line each): the prefix partial at the
     metric workload, dense attention at the LLaDA slice, the reuse path over 8
-    steps, the retained-row pipeline at the sparse workload, and a large block."""
+    steps, the retained-row pipeline at the sparse workload, large blocks and the
+    full-sequence FACache step; `paths` picks a subset."""
     import torch
     import cached_block_attention_amd as ba
 
@@ -148,135 +152,141 @@ def extra_lines(reps: int):
         d["idx"] = up(inp.idx, torch) if inp.idx is not None else None
         return d
 
-    # prefix partial at the metric workload (the state FACache stores)
-    sh = datagen.WORKLOADS["dream_gqa"]
-    t = upl(datagen.make_inputs(sh))
-    alg = algorithmic(sh, with_block=False)
-    pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-    ms = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), reps)
-    emit(path="blkattn_prefix_partial", workload="dream_gqa P32768", ms=round(ms, 4),
-         tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
-    del t, pp
-    torch.cuda.empty_cache()
-
-    # dense attention at the LLaDA slice (fits the 256 MB MALL: timed as is)
-    sh = datagen.WORKLOADS["llada_bf16"]
-    t = upl(datagen.make_inputs(sh))
-    alg = algorithmic(sh)
-    ms = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"]), reps)
-    emit(path="blkattn_full", workload="llada_bf16 P4096", ms=round(ms, 4),
-         tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
-    del t
-    torch.cuda.empty_cache()
-
-    # reuse over 8 denoising steps: prefix partial once, then per step the fused
-    # block step, or block partial + merge, against recomputing full attention
-    sh = datagen.WORKLOADS["reuse_bf16"]
-    inp = datagen.make_inputs(sh)
-    t = upl(inp)
-    steps = [(t["q"], t["k_blk"], t["v_blk"])]
-    for i in range(1, sh.steps):
-        qn, kn, vn = datagen.step_inputs(sh, i)
-        steps.append((up(qn, torch), up(kn, torch), up(vn, torch)))
-    pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-    o = torch.empty_like(t["q"])
-    lse = torch.empty(sh.batch, sh.q_heads, sh.block_len, dtype=torch.float32, device="cuda")
-    pb = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-    ms_prefix = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), max(3, reps // 10))
-    ms_step = float(np.median([_median_ms(lambda s=s: ba.blkattn_block_step(s[0], s[1], s[2], pp, o, lse), reps)
-                               for s in steps]))
-    def two_launch(s):
-        ba.blkattn_block_partial(s[0], s[1], s[2], pb)
-        ba.blkattn_merge(pp, pb, o=o, lse=lse)
-    ms_two = float(np.median([_median_ms(lambda s=s: two_launch(s), reps) for s in steps]))
-    wsf = torch.empty(ba.workspace_bytes(ba.make_dims(t["q"], sh.kv_heads, sh.prefix_len), ba.OP_FULL) + 16,
-                      dtype=torch.uint8, device="cuda")
-    ms_full = _median_ms(lambda: ba.blkattn_full(steps[1][0], t["k_pre"], t["v_pre"], steps[1][1], steps[1][2], o, lse,
-                                                 workspace=wsf), max(3, reps // 10))
-    n = sh.steps
-    emit(path="reuse", workload=f"reuse_bf16 B8 H32 P16384 Bq32, {n} steps", prefix_partial_ms=round(ms_prefix, 4),
-         block_step_ms=round(ms_step, 4), block_partial_plus_merge_ms=round(ms_two, 4),
-         full_recompute_ms=round(ms_full, 4),
-         amortized_ms_per_step=round((ms_prefix + n * ms_step) / n, 4),
-         reuse_gain=round(ms_full / ((ms_prefix + n * ms_step) / n), 2),
-         prefix_partial_hbm_gbps=round(algorithmic(sh, with_block=False)["bytes"] / ms_prefix / 1e6, 1))
-    del t, steps, pp, pb, inp
-    torch.cuda.empty_cache()
-
-    # retained rows at the sparse workload: mass over all 131072 rows, top-k,
-    # standalone gather, and the fused-gather attention over the kept rows
-    sh = datagen.WORKLOADS["sparse_gqa"]
-    inp = datagen.make_inputs(sh)
-    t = upl(inp)
-    _, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
-    mass = torch.empty(sh.batch, sh.kv_heads, sh.prefix_len, dtype=torch.float32, device="cuda")
-    idx = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, dtype=torch.int32, device="cuda")
-    ms_mass = _median_ms(lambda: ba.blkattn_prefix_mass(t["q"], t["k_pre"], lse, mass), reps)
-    sel_dims = ba.Dims(sh.batch, sh.kv_heads, sh.kv_heads, 64, 1, sh.n_keep, sh.prefix_len, ba.F32, 1.0, 0, 0)
-    sel_ws = torch.empty(ba.workspace_bytes(sel_dims, ba.OP_SELECT), dtype=torch.uint8, device="cuda")
-    ms_sel = _median_ms(lambda: ba.blkattn_select_retained(mass, idx, workspace=sel_ws), reps)
-    ko = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, sh.head_dim, dtype=t["k_pre"].dtype, device="cuda")
-    vo = torch.empty_like(ko)
-    ms_gather = _median_ms(lambda: ba.blkattn_gather_prefix(t["k_pre"], t["v_pre"], t["idx"], ko, vo), reps)
-    ms_fused = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"]), reps)
-    G = sh.q_heads // sh.kv_heads
-    mass_flops = 2.0 * sh.batch * sh.kv_heads * G * sh.block_len * sh.prefix_len * sh.head_dim
-    mass_bytes = 2.0 * sh.batch * sh.kv_heads * sh.prefix_len * sh.head_dim + 4.0 * sh.batch * sh.kv_heads * sh.prefix_len
-    alg = algorithmic(sh)
-    gather_bytes = 2 * 2.0 * 2 * sh.batch * sh.kv_heads * sh.n_keep * sh.head_dim
-    emit(path="retention", workload="sparse_gqa B2 Hq28/Hkv4 P_full131072 keep8192 Bq64",
-         mass_ms=round(ms_mass, 4), mass_tflops=round(mass_flops / ms_mass / 1e9, 1),
-         mass_hbm_gbps=round(mass_bytes / ms_mass / 1e6, 1), select_ms=round(ms_sel, 4),
-         gather_ms=round(ms_gather, 4), gather_gbps=round(gather_bytes / ms_gather / 1e6, 1),
-         fused_gather_full_ms=round(ms_fused, 4), fused_tflops=round(alg["flops"] / ms_fused / 1e9, 1))
-    del t, inp, mass, idx, ko, vo
-    torch.cuda.empty_cache()
-
-    # a large block (square, compute-bound bidirectional tile): block partial
-    for bq in (256, 1024):
-        sh = datagen.scaled_shape("llada_bf16", block_len=bq, prefix_len=0)
+    if "prefix" in paths:
+        # prefix partial at the metric workload (the state FACache stores)
+        sh = datagen.WORKLOADS["dream_gqa"]
         t = upl(datagen.make_inputs(sh))
-        pbq = ba.empty_partial(sh.batch, sh.q_heads, bq, sh.head_dim, "cuda")
-        ms = _median_ms(lambda: ba.blkattn_block_partial(t["q"], t["k_blk"], t["v_blk"], pbq), reps)
-        fl = 4.0 * sh.batch * sh.q_heads * bq * bq * sh.head_dim
-        emit(path="blkattn_block_partial", workload=f"large block Bq{bq} B1 H32 d128", ms=round(ms, 4),
-             tflops=round(fl / ms / 1e9, 1), mfma_frac=round(fl / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
-        del t, pbq
+        alg = algorithmic(sh, with_block=False)
+        pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
+        ms = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), reps)
+        emit(path="blkattn_prefix_partial", workload="dream_gqa P32768", ms=round(ms, 4),
+             tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
+        del t, pp
         torch.cuda.empty_cache()
 
-    # full-sequence FACache step (LLaDA-like: 4096 rows, block at rows 2048..2079):
-    # the block's first step builds the cache, later steps reuse it; against
-    # plain attention of every row over every row at each step
-    sh = datagen.WORKLOADS["llada_seq"]
-    B, Hq, N, d, Bq, c0 = sh.batch, sh.q_heads, sh.prefix_len, sh.head_dim, sh.block_len, sh.block_start
-    q, k, v = (up(x, torch) for x in datagen.sequence_inputs(sh, 0))
-    cache = ba.empty_partial(B, Hq, N, d, "cuda")
-    o = torch.empty_like(q)
-    lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
-    dims = ba.Dims(B, Hq, sh.kv_heads, d, Bq, 0, N, ba.BF16, float(sh.scale), 0, 0)
-    ws = torch.empty(max(1, ba.workspace_bytes(dims, ba.OP_SEQUENCE)), dtype=torch.uint8, device="cuda")
-    ms_gen = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, True, o, lse, workspace=ws), reps)
-    ms_step = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, False, o, lse, workspace=ws), reps)
-    full = ba.empty_partial(B, Hq, N, d, "cuda")
-    ms_full = _median_ms(lambda: ba.blkattn_prefix_partial(q, k, v, full), reps)
-    nu = N - Bq
-    fl_gen = 4.0 * B * Hq * (nu * nu + nu * Bq + Bq * N) * d
-    fl_step = 4.0 * B * Hq * (nu * Bq + Bq * N) * d
-    fl_full = 4.0 * B * Hq * N * N * d
-    # a reuse step reads q, the cached (o, m, l) of the other rows and the whole
-    # sequence's k, v (for the block queries), and writes o and lse
-    step_bytes = (2.0 * B * Hq * N * d + 4.0 * B * Hq * nu * (d + 2) + 2 * 2.0 * B * sh.kv_heads * N * d
-                  + 2.0 * B * Hq * N * d + 4.0 * B * Hq * N)
-    n = sh.steps
-    amort = (ms_gen + (n - 1) * ms_step) / n
-    emit(path="blkattn_sequence_step", workload=f"llada_seq B1 H32 d128 N{N} block [{c0},{c0 + Bq}), {n} steps",
-         first_step_ms=round(ms_gen, 4), first_step_tflops=round(fl_gen / ms_gen / 1e9, 1),
-         reuse_step_ms=round(ms_step, 4), reuse_step_tflops=round(fl_step / ms_step / 1e9, 1),
-         reuse_step_hbm_gbps=round(step_bytes / ms_step / 1e6, 1),
-         full_attention_ms=round(ms_full, 4), full_attention_tflops=round(fl_full / ms_full / 1e9, 1),
-         amortized_ms_per_step=round(amort, 4), facache_gain=round(ms_full / amort, 2))
-    del q, k, v, cache, o, lse, ws, full
-    torch.cuda.empty_cache()
+    if "llada" in paths:
+        # dense attention at the LLaDA slice (fits the 256 MB MALL: timed as is)
+        sh = datagen.WORKLOADS["llada_bf16"]
+        t = upl(datagen.make_inputs(sh))
+        alg = algorithmic(sh)
+        ms = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"]), reps)
+        emit(path="blkattn_full", workload="llada_bf16 P4096", ms=round(ms, 4),
+             tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
+        del t
+        torch.cuda.empty_cache()
+
+    if "reuse" in paths:
+        # reuse over 8 denoising steps: prefix partial once, then per step the fused
+        # block step, or block partial + merge, against recomputing full attention
+        sh = datagen.WORKLOADS["reuse_bf16"]
+        inp = datagen.make_inputs(sh)
+        t = upl(inp)
+        steps = [(t["q"], t["k_blk"], t["v_blk"])]
+        for i in range(1, sh.steps):
+            qn, kn, vn = datagen.step_inputs(sh, i)
+            steps.append((up(qn, torch), up(kn, torch), up(vn, torch)))
+        pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(sh.batch, sh.q_heads, sh.block_len, dtype=torch.float32, device="cuda")
+        pb = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
+        ms_prefix = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), max(3, reps // 10))
+        ms_step = float(np.median([_median_ms(lambda s=s: ba.blkattn_block_step(s[0], s[1], s[2], pp, o, lse), reps)
+                                   for s in steps]))
+        def two_launch(s):
+            ba.blkattn_block_partial(s[0], s[1], s[2], pb)
+            ba.blkattn_merge(pp, pb, o=o, lse=lse)
+        ms_two = float(np.median([_median_ms(lambda s=s: two_launch(s), reps) for s in steps]))
+        wsf = torch.empty(ba.workspace_bytes(ba.make_dims(t["q"], sh.kv_heads, sh.prefix_len), ba.OP_FULL) + 16,
+                          dtype=torch.uint8, device="cuda")
+        ms_full = _median_ms(lambda: ba.blkattn_full(steps[1][0], t["k_pre"], t["v_pre"], steps[1][1], steps[1][2], o, lse,
+                                                     workspace=wsf), max(3, reps // 10))
+        n = sh.steps
+        emit(path="reuse", workload=f"reuse_bf16 B8 H32 P16384 Bq32, {n} steps", prefix_partial_ms=round(ms_prefix, 4),
+             block_step_ms=round(ms_step, 4), block_partial_plus_merge_ms=round(ms_two, 4),
+             full_recompute_ms=round(ms_full, 4),
+             amortized_ms_per_step=round((ms_prefix + n * ms_step) / n, 4),
+             reuse_gain=round(ms_full / ((ms_prefix + n * ms_step) / n), 2),
+             prefix_partial_hbm_gbps=round(algorithmic(sh, with_block=False)["bytes"] / ms_prefix / 1e6, 1))
+        del t, steps, pp, pb, inp
+        torch.cuda.empty_cache()
+
+    if "retention" in paths:
+        # retained rows at the sparse workload: mass over all 131072 rows, top-k,
+        # standalone gather, and the fused-gather attention over the kept rows
+        sh = datagen.WORKLOADS["sparse_gqa"]
+        inp = datagen.make_inputs(sh)
+        t = upl(inp)
+        _, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+        mass = torch.empty(sh.batch, sh.kv_heads, sh.prefix_len, dtype=torch.float32, device="cuda")
+        idx = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, dtype=torch.int32, device="cuda")
+        ms_mass = _median_ms(lambda: ba.blkattn_prefix_mass(t["q"], t["k_pre"], lse, mass), reps)
+        sel_dims = ba.Dims(sh.batch, sh.kv_heads, sh.kv_heads, 64, 1, sh.n_keep, sh.prefix_len, ba.F32, 1.0, 0, 0)
+        sel_ws = torch.empty(ba.workspace_bytes(sel_dims, ba.OP_SELECT), dtype=torch.uint8, device="cuda")
+        ms_sel = _median_ms(lambda: ba.blkattn_select_retained(mass, idx, workspace=sel_ws), reps)
+        ko = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, sh.head_dim, dtype=t["k_pre"].dtype, device="cuda")
+        vo = torch.empty_like(ko)
+        ms_gather = _median_ms(lambda: ba.blkattn_gather_prefix(t["k_pre"], t["v_pre"], t["idx"], ko, vo), reps)
+        ms_fused = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"]), reps)
+        G = sh.q_heads // sh.kv_heads
+        mass_flops = 2.0 * sh.batch * sh.kv_heads * G * sh.block_len * sh.prefix_len * sh.head_dim
+        mass_bytes = 2.0 * sh.batch * sh.kv_heads * sh.prefix_len * sh.head_dim + 4.0 * sh.batch * sh.kv_heads * sh.prefix_len
+        alg = algorithmic(sh)
+        gather_bytes = 2 * 2.0 * 2 * sh.batch * sh.kv_heads * sh.n_keep * sh.head_dim
+        emit(path="retention", workload="sparse_gqa B2 Hq28/Hkv4 P_full131072 keep8192 Bq64",
+             mass_ms=round(ms_mass, 4), mass_tflops=round(mass_flops / ms_mass / 1e9, 1),
+             mass_hbm_gbps=round(mass_bytes / ms_mass / 1e6, 1), select_ms=round(ms_sel, 4),
+             gather_ms=round(ms_gather, 4), gather_gbps=round(gather_bytes / ms_gather / 1e6, 1),
+             fused_gather_full_ms=round(ms_fused, 4), fused_tflops=round(alg["flops"] / ms_fused / 1e9, 1))
+        del t, inp, mass, idx, ko, vo
+        torch.cuda.empty_cache()
+
+    if "large" in paths:
+        # a large block (square, compute-bound bidirectional tile): block partial
+        for bq in (256, 1024):
+            sh = datagen.scaled_shape("llada_bf16", block_len=bq, prefix_len=0)
+            t = upl(datagen.make_inputs(sh))
+            pbq = ba.empty_partial(sh.batch, sh.q_heads, bq, sh.head_dim, "cuda")
+            ms = _median_ms(lambda: ba.blkattn_block_partial(t["q"], t["k_blk"], t["v_blk"], pbq), reps)
+            fl = 4.0 * sh.batch * sh.q_heads * bq * bq * sh.head_dim
+            emit(path="blkattn_block_partial", workload=f"large block Bq{bq} B1 H32 d128", ms=round(ms, 4),
+                 tflops=round(fl / ms / 1e9, 1), mfma_frac=round(fl / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
+            del t, pbq
+            torch.cuda.empty_cache()
+
+    if "sequence" in paths:
+        # full-sequence FACache step (LLaDA-like: 4096 rows, block at rows 2048..2079):
+        # the block's first step builds the cache, later steps reuse it; against
+        # plain attention of every row over every row at each step
+        sh = datagen.WORKLOADS["llada_seq"]
+        B, Hq, N, d, Bq, c0 = sh.batch, sh.q_heads, sh.prefix_len, sh.head_dim, sh.block_len, sh.block_start
+        q, k, v = (up(x, torch) for x in datagen.sequence_inputs(sh, 0))
+        cache = ba.empty_partial(B, Hq, N, d, "cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
+        dims = ba.Dims(B, Hq, sh.kv_heads, d, Bq, 0, N, ba.BF16, float(sh.scale), 0, 0)
+        ws = torch.empty(max(1, ba.workspace_bytes(dims, ba.OP_SEQUENCE)), dtype=torch.uint8, device="cuda")
+        ms_gen = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, True, o, lse, workspace=ws), reps)
+        ms_step = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, False, o, lse, workspace=ws), reps)
+        full = ba.empty_partial(B, Hq, N, d, "cuda")
+        ms_full = _median_ms(lambda: ba.blkattn_prefix_partial(q, k, v, full), reps)
+        nu = N - Bq
+        fl_gen = 4.0 * B * Hq * (nu * nu + nu * Bq + Bq * N) * d
+        fl_step = 4.0 * B * Hq * (nu * Bq + Bq * N) * d
+        fl_full = 4.0 * B * Hq * N * N * d
+        # a reuse step reads q, the cached (o, m, l) of the other rows and the whole
+        # sequence's k, v (for the block queries), and writes o and lse
+        step_bytes = (2.0 * B * Hq * N * d + 4.0 * B * Hq * nu * (d + 2) + 2 * 2.0 * B * sh.kv_heads * N * d
+                      + 2.0 * B * Hq * N * d + 4.0 * B * Hq * N)
+        n = sh.steps
+        amort = (ms_gen + (n - 1) * ms_step) / n
+        emit(path="blkattn_sequence_step", workload=f"llada_seq B1 H32 d128 N{N} block [{c0},{c0 + Bq}), {n} steps",
+             first_step_ms=round(ms_gen, 4), first_step_tflops=round(fl_gen / ms_gen / 1e9, 1),
+             reuse_step_ms=round(ms_step, 4), reuse_step_tflops=round(fl_step / ms_step / 1e9, 1),
+             reuse_step_hbm_gbps=round(step_bytes / ms_step / 1e6, 1),
+             full_attention_ms=round(ms_full, 4), full_attention_tflops=round(fl_full / ms_full / 1e9, 1),
+             amortized_ms_per_step=round(amort, 4), facache_gain=round(ms_full / amort, 2))
+        del q, k, v, cache, o, lse, ws, full
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -290,9 +300,11 @@ def main():
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--extra-path", choices=EXTRA_PATHS, action="append",
+                    help="with --extra: only this secondary path (repeatable)")
     ap.add_argument("--extra", action="store_true",
                     help="time the other paths (prefix partial, LLaDA slice, reuse steps, retention, "
-                         "large block) instead of the metric line")
+                         "large blocks, full-sequence step) instead of the metric line")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_bf16_dream_gqa_traffic.json"),
                     help="JSON record of the attention kernel's measured HBM bytes per launch "
                          "(used only while its kernel-source hash matches the current source)")
@@ -309,7 +321,7 @@ def main():
         copy_probe()
         return
     if args.extra:
-        extra_lines(max(10, args.steps // 10))
+        extra_lines(max(10, args.steps // 10), tuple(args.extra_path or EXTRA_PATHS))
         return
     import cached_block_attention_amd as ba
     ba.library()

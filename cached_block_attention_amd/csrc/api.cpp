@@ -587,9 +587,7 @@ int blkattn_prefix_mass(const blkattn_dims* d, const blkattn_tensor* q, const bl
   if (lse == nullptr) return fail(BLKATTN_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return fail(BLKATTN_ERR_MISALIGNED, "lse is not 4-byte aligned");
   const int64_t R = (int64_t)(d->q_heads / d->kv_heads) * d->block_len;
-  if (d->dtype == BLKATTN_BF16 && R > mass_max_rows())
-    return fail(BLKATTN_ERR_UNSUPPORTED, "q_heads/kv_heads * block_len = %lld exceeds %d rows per kv head",
-                (long long)R, mass_max_rows());
+  if (R > INT32_MAX) return fail(BLKATTN_ERR_UNSUPPORTED, "too many query rows per kv head");
   MassParams p{};
   p.batch = d->batch, p.q_heads = d->q_heads, p.kv_heads = d->kv_heads, p.group = d->q_heads / d->kv_heads;
   p.head_dim = d->head_dim, p.block_len = d->block_len, p.dtype = d->dtype;

@@ -125,6 +125,8 @@ struct MassParams {
   float scale_log2;
   int32_t splits;               // bf16: key splits (gridDim.x)
   int32_t tiles;                // bf16: ceil(n_keys / mass_tile_keys())
+  int32_t row0, row_end;        // bf16: packed rows of this pass (set by the launcher)
+  int32_t accumulate;           // bf16: add onto mass (passes after the first)
 };
 
 // Kernel launchers (return the hipError_t of the launch).
@@ -145,7 +147,6 @@ struct SelectPlan {
 SelectPlan select_plan(int64_t groups, int64_t n);
 hipError_t launch_select(const float* mass, int32_t* idx, void* ws, int64_t groups, int64_t n, int64_t k,
                          hipStream_t stream);
-int mass_max_rows();   // largest G * Bq the bf16 mass kernel supports
 int mass_tile_keys();  // keys per tile of the bf16 mass kernel
 
 // Launch shape of the bf16 kernel: waves per workgroup for a chunk of packed

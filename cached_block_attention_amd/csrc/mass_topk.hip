@@ -44,24 +44,13 @@ __device__ __forceinline__ int mswz(int r) {
   return CPR == 16 ? (r & 15) : ((r ^ (r >> 3)) & 7);
 }
 
-// One halving step of the column sum over the 32 lanes of a wave half: lanes
-// whose bit M is set keep registers M..2M-1 (summed with the partner lane's),
-// the others registers 0..M-1; after the steps 16, 8, 4, 2, 1 lane n holds the
-// total of register n over the 32 lanes.
-template <int M>
-__device__ __forceinline__ void halve_sum(float* v, int n) {
-  const bool upper = (n & M) != 0;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    const float send = upper ? v[i] : v[i + M];
-    const float keep = upper ? v[i + M] : v[i];
-    v[i] = keep + __shfl_xor(send, M);
-  }
-  if constexpr (M > 1) halve_sum<M / 2>(v, n);
-}
-
-// bf16: one workgroup of 8 waves per (key split, batch * kv head); wave w owns
-// the 32-row blocks w, w + 8, ... (RBW of them) of the G * Bq packed rows.
+// bf16: one workgroup of 8 waves per (key split, batch * kv head) and pass of
+// up to 32 * 8 * RBW packed rows; wave w owns the 32-row blocks w, w + 8, ...
+// (RBW of them) of the pass. Scores come out as S = Q K^T (query rows in the
+// M dimension of v_mfma_f32_32x32x16_bf16, keys in N), so a lane holds one key
+// column: its 16 accumulator registers are 16 of the block's rows, and the
+// column sum is an in-register sum plus one exchange between the wave halves.
+// Each K fragment read from LDS feeds every row block of the wave.
 template <int D, int RBW>
 __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassParams p) {
   constexpr int NW = kMassWaves, TK = kMassTile;
@@ -90,29 +79,47 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
   const int t1 = (int)((int64_t)(split + 1) * p.tiles / p.splits);
   const float c2 = p.scale_log2;
 
-  // query fragments and -LSE (base 2) of this wave's rows; rows past R get
-  // -inf, so their weights are exactly 0
+  // A-operand query fragments (row n of each block) and, for the 16 rows the
+  // accumulator registers hold (row 8 (r / 4) + 4 h + r % 4 of the block),
+  // -LSE in base 2; rows past R get -inf, so their weights are exactly 0
   bf16x8_t qf[RBW][KPB];
-  float nl2[RBW];
+  float nl2[RBW][16];
   bool has[RBW];
+  auto row_of = [&](int prow, int& hq, int& qi) __attribute__((always_inline)) {
+    const int g = prow / p.block_len;
+    qi = prow - g * p.block_len;
+    hq = hkv * p.group + g;
+  };
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
-    const int rb = wave + NW * j;
-    has[j] = 32 * rb < R;  // wave-uniform
-    const int prow = 32 * rb + n;
-    const bool ok = prow < R;
-    const int g = ok ? prow / p.block_len : 0;
-    const int qi = ok ? prow - g * p.block_len : 0;
-    const int hq = hkv * p.group + g;
-    const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + hq * p.q_sh + qi * p.q_st;
+    const int rb0 = p.row0 + 32 * (wave + NW * j);  // first packed row of the block
+    has[j] = rb0 < p.row_end;                        // wave-uniform
+    {
+      const int prow = rb0 + n;
+      const bool ok = prow < p.row_end;
+      int hq = 0, qi = 0;
+      if (ok) row_of(prow, hq, qi);
+      const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + hq * p.q_sh + qi * p.q_st;
 #pragma unroll
-    for (int kk = 0; kk < KPB; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok) v = *(const uint4*)(qrow + 16 * kk + 8 * h);
-      qf[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      for (int kk = 0; kk < KPB; ++kk) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = *(const uint4*)(qrow + 16 * kk + 8 * h);
+        qf[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
-    nl2[j] = ok ? -p.lse[((int64_t)b * p.q_heads + hq) * p.block_len + qi] * kLog2eM : -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int prow = rb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      float v = -INFINITY;
+      if (prow < p.row_end) {
+        int hq, qi;
+        row_of(prow, hq, qi);
+        v = -p.lse[((int64_t)b * p.q_heads + hq) * p.block_len + qi] * kLog2eM;
+      }
+      nl2[j][r] = v;
+    }
   }
+  (void)R;
 
   // K tile t: thread tid stages chunks tid + 512 * i; rows past the prefix read
   // row 0 (their mass is never written)
@@ -138,8 +145,6 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
     }
   };
 
-  // lane (h, n) ends the reduction with the column of register n: key
-  const int kid = 32 * (n >> 4) + 8 * ((n & 15) >> 2) + 4 * h + (n & 3);
   float* mrow = p.mass + ((int64_t)b * p.kv_heads + hkv) * p.n_keys;
 
   if (t0 < t1) {
@@ -151,39 +156,49 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
     const int cur = (t - t0) & 1;
     if (t + 1 < t1) load_tile(t + 1);  // in flight while this tile is computed
     const char* kb = kbuf[cur];
-    float acc = 0.0f;
+    f32x16_t sacc[RBW][NSB];
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      if (!has[j]) continue;
-      f32x16_t sacc[NSB];
+    for (int j = 0; j < RBW; ++j)
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[j][sb][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KPB; ++kk)
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.0f;
         const int krow = 32 * sb + n;
+        const uint4 a = *(const uint4*)(kb + krow * ROWB + 16 * ((2 * kk + h) ^ mswz<CPR>(krow)));
 #pragma unroll
-        for (int kk = 0; kk < KPB; ++kk) {
-          const uint4 a = *(const uint4*)(kb + krow * ROWB + 16 * ((2 * kk + h) ^ mswz<CPR>(krow)));
-          sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[j][kk],
-                                                             sacc[sb], 0, 0, 0);
-        }
+        for (int j = 0; j < RBW; ++j)
+          if (has[j])
+            sacc[j][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j][kk], __builtin_bit_cast(bf16x8_t, a),
+                                                                  sacc[j][sb], 0, 0, 0);
       }
-      float v[32];
+    // column sums: key 32 sb + n over this wave's rows, fixed order (j, r)
+    float cs[NSB];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 4][i & 15], c2, nl2[j]));
-      // sum over the 32 rows (lanes n of this half); lane n keeps register n's
-      // column total
-      halve_sum<16>(v, n);
-      acc += v[0];
+    for (int sb = 0; sb < NSB; ++sb) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < RBW; ++j)
+        if (has[j]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += __builtin_amdgcn_exp2f(fmaf(sacc[j][sb][r], c2, nl2[j][r]));
+        }
+      cs[sb] = acc + __shfl_xor(acc, 32);  // the other half's 16 rows of each block
     }
-    red[wave][kid] = acc;
+    if (h == 0) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) red[wave][32 * sb + n] = cs[sb];
+    }
     __syncthreads();  // red complete; every wave is done with kbuf[cur]
     if (wave == 0) {
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += red[w][lane];
       const int64_t key = (int64_t)t * TK + lane;
-      if (key < p.n_keys) mrow[key] = s;
+      if (key < p.n_keys) mrow[key] = p.accumulate ? mrow[key] + s : s;
     }
     if (t + 1 < t1) store_tile(cur ^ 1);
     __syncthreads();  // next tile staged; red read
@@ -424,23 +439,29 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(SelParams p) 
 }
 
 template <int D>
-hipError_t launch_mass_d(const MassParams& p, hipStream_t stream) {
-  const int R = p.group * p.block_len;
-  const int rbw = (R + 32 * kMassWaves - 1) / (32 * kMassWaves);  // row blocks per wave
-  dim3 grid(p.splits, p.batch * p.kv_heads);
-  switch (rbw) {
-    case 1: hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), grid, dim3(64 * kMassWaves), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), grid, dim3(64 * kMassWaves), 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((mass_bf16_kernel<D, 3>), grid, dim3(64 * kMassWaves), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((mass_bf16_kernel<D, 4>), grid, dim3(64 * kMassWaves), 0, stream, p); break;
-    default: return hipErrorInvalidValue;
+hipError_t launch_mass_d(const MassParams& p0, hipStream_t stream) {
+  const int R = p0.group * p0.block_len;
+  constexpr int kPassRows = 32 * kMassWaves * 2;
+  dim3 grid(p0.splits, p0.batch * p0.kv_heads);
+  // passes over the packed rows run in order on the stream; later passes add
+  // their column sums onto the earlier ones (fixed order: reproducible)
+  for (int row0 = 0; row0 < R; row0 += kPassRows) {
+    MassParams p = p0;
+    p.row0 = row0;
+    p.row_end = row0 + kPassRows < R ? row0 + kPassRows : R;
+    p.accumulate = row0 > 0;
+    if (p.row_end - row0 > 32 * kMassWaves)
+      hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), grid, dim3(64 * kMassWaves), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), grid, dim3(64 * kMassWaves), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
 
-int mass_max_rows() { return 32 * kMassWaves * 4; }
 int mass_tile_keys() { return kMassTile; }
 
 hipError_t launch_mass(const MassParams& p, hipStream_t stream) {

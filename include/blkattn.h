@@ -266,8 +266,9 @@ int blkattn_sequence_step(const blkattn_dims* dims, int64_t block_start, int gen
  *   lse    fp32 [B, Hq, Bq] contiguous: each row's log-sum-exp over all keys it
  *          attends (as blkattn_full returns it)
  *   mass   fp32 [B, Hkv, prefix_len] contiguous output
- * bf16 supports q_heads / kv_heads * block_len <= 1024. The column sums run in
- * a fixed order (bitwise reproducible).
+ * The column sums run in a fixed order (bitwise reproducible); with more than
+ * 512 query rows per kv head (q_heads / kv_heads * block_len) the rows are
+ * taken in passes of 512 launched in order on `stream`.
  */
 int blkattn_prefix_mass(const blkattn_dims* dims, const blkattn_tensor* q, const blkattn_tensor* k_pre,
                         const float* lse, float* mass, void* stream);

@@ -43,6 +43,8 @@ CASES = [
     ("llada_bf16", dict(q_heads=3, kv_heads=3, prefix_len=700)),                    # 32 rows
     ("dream_gqa", dict(batch=1, q_heads=6, kv_heads=2, prefix_len=333, block_len=20, head_dim=64)),
     ("dream_gqa", dict(batch=1, q_heads=16, kv_heads=1, prefix_len=200, block_len=64)),  # 1024 rows
+    ("dream_gqa", dict(batch=1, q_heads=8, kv_heads=1, prefix_len=300, block_len=75)),   # 600 rows: 2 passes
+    ("dream_gqa", dict(batch=1, q_heads=16, kv_heads=2, prefix_len=130, block_len=200)),  # 1600 rows: 4 passes
 ]
 
 

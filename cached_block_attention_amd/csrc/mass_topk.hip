@@ -245,6 +245,19 @@ __global__ __launch_bounds__(64) void mass_f32_kernel(const MassParams p) {
 // those matching it); state[4] = (T, ties taken).
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxChunks = 32;
+constexpr int kSelBatch = 16;  // rows per thread loaded before any is used
+
+// Rows base + i * kSelThreads + threadIdx.x (i < kSelBatch) of a group's
+// masses below `end`, as ordered keys; rows at or past `end` read as 0.
+__device__ __forceinline__ void sel_load(const uint32_t* row, int64_t base, int64_t end, uint32_t* xs) {
+#pragma unroll
+  for (int i = 0; i < kSelBatch; ++i) {
+    const int64_t j = base + (int64_t)i * kSelThreads + threadIdx.x;
+    xs[i] = j < end ? row[j] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kSelBatch; ++i) xs[i] = xs[i] == 0x80000000u ? 0u : xs[i];
+}
 
 struct SelParams {
   const uint32_t* bits;  // [G, n]
@@ -256,8 +269,6 @@ struct SelParams {
   int groups, chunks;
 };
 
-__device__ __forceinline__ uint32_t sel_key(uint32_t x) { return x == 0x80000000u ? 0u : x; }
-
 // From the previous pass's state and its per-chunk histograms, the digit of T
 // at `shift` and the state after it. Every thread returns the same values.
 __device__ void sel_derive(const SelParams& p, int g, int pass_prev, uint32_t prev_prefix, uint32_t prev_need,
@@ -268,8 +279,14 @@ __device__ void sel_derive(const SelParams& p, int g, int pass_prev, uint32_t pr
     s_out[1] = prev_need;
   }
   const uint32_t* h = p.hist + ((int64_t)pass_prev * p.groups + g) * p.chunks * 256;
+  // every chunk's bin in flight at once (clamped indices keep the loads in
+  // bounds and the code straight-line), then summed in chunk order
+  uint32_t hv[kSelMaxChunks];
+#pragma unroll
+  for (int ch = 0; ch < kSelMaxChunks; ++ch) hv[ch] = h[(ch < p.chunks ? ch : p.chunks - 1) * 256 + tid];
   uint32_t c = 0;
-  for (int ch = 0; ch < p.chunks; ++ch) c += h[ch * 256 + tid];
+#pragma unroll
+  for (int ch = 0; ch < kSelMaxChunks; ++ch) c += ch < p.chunks ? hv[ch] : 0u;
   s_bins[tid] = c;
   __syncthreads();
   // inclusive suffix sums: s_bins[t] = rows whose digit is >= t
@@ -297,6 +314,11 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelParams p, i
   const int tid = threadIdx.x, lane = tid & 63;
   const int c = blockIdx.x, g = blockIdx.y;
   if (p.k >= p.n) return;
+  const uint32_t* row = p.bits + (int64_t)g * p.n;
+  const int64_t j0 = (int64_t)c * p.chunk;
+  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
+  uint32_t xs[kSelBatch];
+  sel_load(row, j0, j1, xs);  // in flight while the digit so far is derived
   uint32_t prefix = 0, need = (uint32_t)p.k;
   if (pass > 0) {
     uint32_t pp = 0, pn = (uint32_t)p.k;
@@ -314,25 +336,26 @@ __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(SelParams p, i
   __syncthreads();
   const int shift = 24 - 8 * pass;
   const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-  const uint32_t* row = p.bits + (int64_t)g * p.n;
-  const int64_t j0 = (int64_t)c * p.chunk;
-  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
-  for (int64_t j = j0 + tid; j - tid < j1; j += kSelThreads) {
-    const bool in = j < j1;
-    const uint32_t x = in ? sel_key(row[j]) : 0u;
-    const bool m = in && (x & hmask) == prefix;
-    const uint32_t dg = (x >> shift) & 255u;
-    // the wave's most common case (all rows in one bin) becomes a single atomic
-    const uint64_t act = __ballot(m);
-    if (act != 0) {
-      const int lead = __ffsll((unsigned long long)act) - 1;
-      const uint32_t d0 = __shfl(dg, lead);
-      const bool same = m && dg == d0;
-      const uint64_t smask = __ballot(same);
-      if (same) {
-        if (lane == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(smask));
-      } else if (m) {
-        atomicAdd(&s_hist[dg], 1u);
+  for (int64_t base = j0; base < j1; base += (int64_t)kSelThreads * kSelBatch) {
+    if (base != j0) sel_load(row, base, j1, xs);
+#pragma unroll
+    for (int i = 0; i < kSelBatch; ++i) {
+      const int64_t j = base + (int64_t)i * kSelThreads + tid;
+      const uint32_t x = xs[i];
+      const bool m = j < j1 && (x & hmask) == prefix;
+      const uint32_t dg = (x >> shift) & 255u;
+      // the wave's most common case (all rows in one bin) becomes a single atomic
+      const uint64_t act = __ballot(m);
+      if (act != 0) {
+        const int lead = __ffsll((unsigned long long)act) - 1;
+        const uint32_t d0 = __shfl(dg, lead);
+        const bool same = m && dg == d0;
+        const uint64_t smask = __ballot(same);
+        if (same) {
+          if (lane == lead) atomicAdd(&s_hist[d0], (uint32_t)__popcll(smask));
+        } else if (m) {
+          atomicAdd(&s_hist[dg], 1u);
+        }
       }
     }
   }
@@ -347,6 +370,11 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, g = blockIdx.y;
   if (p.k >= p.n) return;
+  const uint32_t* row = p.bits + (int64_t)g * p.n;
+  const int64_t j0 = (int64_t)c * p.chunk;
+  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
+  uint32_t xs[kSelBatch];
+  sel_load(row, j0, j1, xs);  // in flight while T is derived
   uint32_t T, ties;
   sel_derive(p, g, 3, p.state[(3 * p.groups + g) * 2], p.state[(3 * p.groups + g) * 2 + 1], s_bins, s_out, T,
              ties);
@@ -354,14 +382,15 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(SelParams p) 
     p.state[(4 * p.groups + g) * 2] = T;
     p.state[(4 * p.groups + g) * 2 + 1] = ties;
   }
-  const uint32_t* row = p.bits + (int64_t)g * p.n;
-  const int64_t j0 = (int64_t)c * p.chunk;
-  const int64_t j1 = j0 + p.chunk < p.n ? j0 + p.chunk : p.n;
   uint32_t gt = 0, eq = 0;
-  for (int64_t j = j0 + tid; j < j1; j += kSelThreads) {
-    const uint32_t x = sel_key(row[j]);
-    gt += x > T ? 1u : 0u;
-    eq += x == T ? 1u : 0u;
+  for (int64_t base = j0; base < j1; base += (int64_t)kSelThreads * kSelBatch) {
+    if (base != j0) sel_load(row, base, j1, xs);
+#pragma unroll
+    for (int i = 0; i < kSelBatch; ++i) {
+      const bool in = base + (int64_t)i * kSelThreads + tid < j1;
+      gt += in && xs[i] > T ? 1u : 0u;
+      eq += in && xs[i] == T ? 1u : 0u;
+    }
   }
   for (int off = 32; off >= 1; off >>= 1) {
     gt += __shfl_xor(gt, off);
@@ -391,13 +420,21 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(SelParams p) 
     for (int64_t j = j0 + tid; j < j1; j += kSelThreads) out[j] = (int32_t)j;
     return;
   }
+  const uint32_t* row = p.bits + (int64_t)g * p.n;
+  uint32_t xs[kSelBatch];
+  sel_load(row, j0, j1, xs);
   const uint32_t T = p.state[(4 * p.groups + g) * 2];
   const int64_t ties = p.state[(4 * p.groups + g) * 2 + 1];
+  // rows above T and equal to T in the chunks before this one: every count in
+  // flight at once (clamped, straight-line), summed in chunk order
+  uint2 cv[kSelMaxChunks];
+#pragma unroll
+  for (int ch = 0; ch < kSelMaxChunks; ++ch)
+    cv[ch] = *(const uint2*)(p.counts + ((int64_t)g * p.chunks + (ch < c ? ch : 0)) * 2);
   int64_t gt_before = 0, eq_before = 0;
-  for (int ch = 0; ch < c; ++ch) {
-    gt_before += p.counts[((int64_t)g * p.chunks + ch) * 2];
-    eq_before += p.counts[((int64_t)g * p.chunks + ch) * 2 + 1];
-  }
+#pragma unroll
+  for (int ch = 0; ch < kSelMaxChunks; ++ch)
+    if (ch < c) gt_before += cv[ch].x, eq_before += cv[ch].y;
   auto clamp_take = [](int64_t avail, int64_t cnt) -> int64_t {  // min(max(avail, 0), cnt)
     return avail <= 0 ? 0 : (avail < cnt ? avail : cnt);
   };
@@ -406,9 +443,13 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(SelParams p) 
   const uint64_t lt = (1ull << lane) - 1ull;
   int it = 0;
   for (int64_t jb = j0; jb < j1; jb += kSelThreads, ++it) {
+    const int bi = it % kSelBatch;
+    if (bi == 0 && jb != j0) sel_load(row, jb, j1, xs);
     const int64_t j = jb + tid;
     const bool in = j < j1;
-    const uint32_t x = in ? sel_key(p.bits[(int64_t)g * p.n + j]) : 0u;
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < kSelBatch; ++i) x = i == bi ? xs[i] : x;  // register select, no scratch
     const bool gt = in && x > T;
     const bool eq = in && x == T;
     const uint64_t gm = __ballot(gt), em = __ballot(eq);

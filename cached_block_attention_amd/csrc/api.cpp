@@ -173,6 +173,8 @@ void fill_keys(KeySeq& ks, const blkattn_dims* d, const blkattn_tensor* k_pre, c
     ks.kp_sb = k_pre->stride_b, ks.kp_sh = k_pre->stride_h, ks.kp_st = k_pre->stride_t;
     ks.v_pre = v_pre->data;
     ks.vp_sb = v_pre->stride_b, ks.vp_sh = v_pre->stride_h, ks.vp_st = v_pre->stride_t;
+    const int64_t st = (ks.kp_st > ks.vp_st ? ks.kp_st : ks.vp_st) * elt_bytes(d->dtype);
+    ks.off32 = st <= ((int64_t)1 << 25);  // 64 rows of the tile plus a row stay below 2^31 bytes
   }
   if (n_blk > 0) {
     ks.k_blk = k_blk->data;

@@ -18,9 +18,10 @@
 //    kv-head and split (GQA packing).
 //  * K/V tiles stream HBM -> LDS with direct-to-LDS DMA loads
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no
-//    register staging) into a ring of NS stages, so NS-1 tiles are in flight
-//    while one is computed; one barrier per tile. Rows are stored with an XOR
-//    swizzle of their 16-byte chunks, chosen on the global side of the DMA.
+//    register staging) into rings of LDS tiles, several tiles in flight. Rows
+//    are stored with an XOR swizzle of their 16-byte chunks, chosen on the
+//    global side of the DMA. Inside a dense prefix the source is a scalar tile
+//    base plus a per-lane 32-bit offset fixed for the whole loop.
 //  * Each wave owns 32 packed rows. Scores are computed transposed,
 //    S^T = K Q^T (v_mfma_f32_32x32x16_bf16; keys on the M side read from LDS,
 //    queries on the N side held in registers for the whole loop), so a lane
@@ -38,6 +39,12 @@
 //    sum of those rounded weights (v_dot2_f32_bf16 against (1, 1)), so o is an
 //    exact convex combination of V rows with the weights actually used; l and
 //    the log-sum-exp use the sum of the unrounded weights.
+//  * Eight-wave workgroups (more than 128 packed rows) run the two halves of
+//    the workgroup half a tile apart ("ping-pong"): waves 0-3 and 4-7 share
+//    the four SIMDs pairwise, and while one wave of a pair issues the MFMAs of
+//    a tile (PV of the previous tile, then the scores of this one) the other
+//    runs the softmax of its tile on the vector ALU. The matrix cores and the
+//    vector ALU of a SIMD then work at the same time instead of in turn.
 #include "launch.h"
 
 #include <math.h>
@@ -70,6 +77,15 @@ __device__ __forceinline__ int swz_v(int r) {
   return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
+// max(a, b, c) as one v_max3_f32. fmaxf() would first quiet possible
+// signalling NaNs of MFMA results (one extra v_max per operand); scores are
+// never NaN here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -87,30 +103,25 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `ahead` later stages of this wave's DMAs are in flight.
-template <int IPW, int NS>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if (NS >= 4 && ahead >= 2) wait_vm<(NS >= 4 ? 2 : 0) * IPW>();
-  else if (NS >= 3 && ahead >= 1) wait_vm<(NS >= 3 ? 1 : 0) * IPW>();
-  else wait_vm<0>();
-}
-
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would drain every outstanding DMA (vmcnt(0)) at each tile. LDS data is
 // ordered explicitly instead: DMA completion by s_waitcnt vmcnt before the
 // barrier, and every LDS read of a tile is consumed by an MFMA before the
-// barrier that lets its ring slot be refilled.
+// barrier that lets its slot be refilled. The scheduling barriers keep the
+// compiler from moving any instruction across it.
 __device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One direct-to-LDS DMA: 64 lanes x 16 bytes from per-lane global addresses
 // into 1 KB of LDS at lds_addr (wave-uniform, through M0). Written as inline
 // asm so that the compiler does not see an LDS write in flight and drain the
 // whole DMA ring (vmcnt(0)) before every LDS read; completion is ordered
-// explicitly by wait_stage() before the tile barrier. The instruction has no
+// explicitly by vmcnt waits before the tile barriers. The instruction has no
 // register results.
 __device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
   __asm__ __volatile__(
@@ -121,30 +132,411 @@ __device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
       : "memory", "m0");
 }
 
+// The same DMA from a wave-uniform base in scalar registers plus a per-lane
+// unsigned 32-bit byte offset.
+__device__ __forceinline__ void dma_1k_s(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+      : "memory", "m0");
+}
+
+// A wave-uniform pointer moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* q) {
+  const uint64_t v = (uint64_t)(uintptr_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 constexpr int kIdxCap = 2048;  // retained-row indices staged per split
 
-template <int D, int NW, int TK, int NS>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) {
-  constexpr int ROWB = D * 2;              // bytes per K/V row
-  constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
-  constexpr int KBYTES = TK * ROWB;        // K part of a stage
-  constexpr int STB = 2 * KBYTES;          // bytes per stage (K then V)
-  constexpr int INS = STB / 1024;          // DMA instructions per stage
-  constexpr int IPW = INS / NW;            // per wave
-  constexpr int RPI = 1024 / ROWB;         // rows per DMA instruction
-  constexpr int NSB = TK / 32;             // 32-key score blocks per tile
-  constexpr int NCC = TK / 16;             // 16-key chunks of the PV product
-  constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O^T
-  static_assert(INS % NW == 0, "every wave issues the same number of DMAs");
-  static_assert(IPW * (NS - 2) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char ring[NS * STB];
-  __shared__ int32_t sidx[kIdxCap];
+// The key sequence of one (batch, kv-head), in bytes.
+struct KeyRows {
+  const char* kpre;
+  const char* vpre;
+  const char* kblk;
+  const char* vblk;
+  int64_t kp_st, vp_st, kb_st, vb_st;  // row strides in bytes
+  int64_t n_pre, n_all, hole, hole_len;
+  bool indexed, off32;
+};
 
+// A value hidden from the optimiser: what is computed from it is recomputed
+// where it is used instead of being hoisted out of the tile loop and kept in
+// registers (or spilled) through it.
+__device__ __forceinline__ int opaque(int x) {
+  __asm__ __volatile__("" : "+v"(x));
+  return x;
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)LDS_PTR(const char, ptr);
+}
+
+// DMA instruction k of the K (isv = false) or V rows of one TK-key tile
+// starting at key key0, into the LDS tile at byte address dst (TK * 2D bytes,
+// TK*2D/1024 instructions of 1 KB). Instruction k covers tile rows
+// k*RPI .. k*RPI + RPI - 1; lane t fills LDS chunk t % CPR of its row with
+// logical chunk (t % CPR) ^ swizzle(row). Keys past the end of the sequence
+// read a valid row (their weight is 0); retained-row indices come from sidx
+// (this split's, from key kbeg on). Inside the dense prefix, with 32-bit tile
+// offsets, the source is a scalar tile base plus a per-lane offset.
+template <int TK>
+__device__ __forceinline__ bool tile_is_fast(const KeyRows& kr, int64_t key0) {
+  return !kr.indexed && key0 + TK <= kr.n_pre && kr.off32 && (key0 + TK <= kr.hole || key0 >= kr.hole);
+}
+
+template <int D, int TK>
+__device__ __forceinline__ void dma_one_fast(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k,
+                                             int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPI = 1024 / ROWB;
+  const int64_t row0 = key0 + (key0 >= kr.hole ? kr.hole_len : 0);
+  const int64_t st = isv ? kr.vp_st : kr.kp_st;
+  const char* sbase = uniform_ptr((isv ? kr.vpre : kr.kpre) + row0 * st);
+  const int ln = opaque(lane);
+  const int r = k * RPI + ln / CPR;
+  const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+  dma_1k_s(sbase, (uint32_t)r * (uint32_t)st + 16 * lc, dst + k * 1024);
+}
+
+template <int D, int TK>
+__device__ __forceinline__ void dma_one(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k, int lane,
+                                        const int32_t* sidx, int64_t kbeg) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPI = 1024 / ROWB;
+  if (tile_is_fast<TK>(kr, key0)) {
+    dma_one_fast<D, TK>(kr, isv, key0, dst, k, lane);
+    return;
+  }
+  const bool dense = !kr.indexed && key0 + TK <= kr.n_pre;
+  const int r = k * RPI + lane / CPR;
+  const int lc = (lane % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+  const char* base = isv ? kr.vpre : kr.kpre;
+  int64_t st = isv ? kr.vp_st : kr.kp_st;
+  int64_t row = key0 + r;
+  if (dense) {
+    row += row >= kr.hole ? kr.hole_len : 0;
+  } else {
+    const int64_t key = row < kr.n_all ? row : kr.n_all - 1;
+    if (key < kr.n_pre) {
+      row = kr.indexed ? (int64_t)sidx[key - kbeg] : key + (key >= kr.hole ? kr.hole_len : 0);
+    } else {
+      row = key - kr.n_pre;
+      base = isv ? kr.vblk : kr.kblk;
+      st = isv ? kr.vb_st : kr.kb_st;
+    }
+  }
+  dma_1k(base + row * st + 16 * lc, dst + k * 1024);
+}
+
+// The whole DMA of one K (or V) tile, issued by one wave. On the fast path
+// each instruction is a scalar base plus a per-lane offset recomputed from the
+// lane index (a few VALU operations, no registers held across the loop); the
+// other tiles loop over the general form without unrolling it.
+template <int D, int TK>
+__device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int lane,
+                                             const int32_t* sidx, int64_t kbeg) {
+  constexpr int INT = TK * D * 2 / 1024;
+  if (tile_is_fast<TK>(kr, key0)) {
+#pragma unroll
+    for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(kr, isv, key0, dst, k, lane);
+    return;
+  }
+#pragma unroll 1
+  for (int k = 0; k < INT; ++k) dma_one<D, TK>(kr, isv, key0, dst, k, lane, sidx, kbeg);
+}
+
+// This wave's share of the DMA of one K (or V) tile: with NW waves issuing,
+// wave w issues instructions w*IPW .. w*IPW + IPW - 1.
+template <int D, int TK, int NW>
+__device__ __forceinline__ void dma_tile(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int wave,
+                                         int lane, const int32_t* sidx, int64_t kbeg) {
+  constexpr int IPW = TK * D * 2 / 1024 / NW;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) dma_one<D, TK>(kr, isv, key0, dst, wave * IPW + j, lane, sidx, kbeg);
+}
+
+// S^T = K Q^T for one tile: sacc[sb] holds keys 32*sb + 8*(r/4) + 4*h + r%4
+// (register r) against this lane's query. The K operands are read from LDS
+// two head-dim steps ahead of their MFMAs; the scheduling barriers keep the
+// compiler from hoisting every read of the tile (which would need 64 more
+// registers).
+template <int D, int TK>
+__device__ __forceinline__ void tile_scores(f32x16_t (&sacc)[TK / 32], const char* kb,
+                                            const bf16x8_t (&qf)[D / 16], int n, int h) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int NSB = TK / 32;
+  constexpr int NK = D / 16;
+  constexpr int PF = 1;
+  // Row r = 32*sb + n at logical chunk 2*kk + h sits at byte
+  // r*ROWB + 16*((2*kk + h) ^ swz(r)) = (r*ROWB + 16*(h ^ swz(r))) ^ (32*kk):
+  // the chunk bits lie below the row bits, so one XOR per step.
+  int kbase[NSB];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const int r = 32 * sb + n;
+    kbase[sb] = opaque(r * ROWB + 16 * (h ^ swz_k<CPR>(r)));
+  }
+  uint4 ka[PF + 1][NSB];
+  auto load = [&](int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) ka[kk % (PF + 1)][sb] = *(const uint4*)(kb + (kbase[sb] ^ (32 * kk)));
+  };
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < PF && kk < NK; ++kk) load(kk);
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    if (kk + PF < NK) load(kk + PF);
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+      sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[kk % (PF + 1)][sb]),
+                                                         qf[kk], sacc[sb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Adds the bf16 weights of chunk pb (8 keys of this lane) to the four partial
+// sums lh. v_dot2_f32_bf16 against (1, 1) sums two weights exactly as the PV
+// product sees them.
+__device__ __forceinline__ void sum_bf16_weights(float (&lh)[4], const bf16x8_t& pb) {
+  bf16x2_t one;
+  one[0] = (__bf16)1.0f;
+  one[1] = (__bf16)1.0f;
+  lh[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, lh[0], false);
+  lh[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, lh[1], false);
+  lh[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, lh[2], false);
+  lh[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, lh[3], false);
+}
+
+// Running online-softmax state of one lane's query row.
+template <int D>
+struct RowState {
+  f32x16_t oacc[D / 32];  // O~^T: head dims 32*db + 8*(r/4) + 4*h + r%4
+  float m2;               // reference max (base 2) shared by l and O~
+  float mtrue;            // exact running max (base 2)
+  float lsum;             // lane-partial sum of the weights
+  float lhat;             // lane-partial sum of the bf16-rounded weights
+};
+
+// Eqs. 2-5 for one tile: mask keys past `nvalid`, move the reference max if
+// needed (rescaling O~ and the sums), weights P~ = 2^(s*c2 - m2) into the sum
+// l and, rounded to bf16, into the PV operand pb (chunk cc: 16 keys). With
+// LHAT the rounded weights are also summed here; otherwise the caller adds
+// them (with sum_bf16_weights) where the PV product consumes pb.
+template <int D, int TK, bool LHAT>
+__device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t (&pb)[TK / 16],
+                                             RowState<D>& st, float c2, int64_t nvalid, int h) {
+  constexpr int NSB = TK / 32;
+  if (nvalid < TK) {
+    const int nv = (int)nvalid;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= nv) sacc[sb][r] = -INFINITY;
+      }
+  }
+  // Four independent chains in every reduction: a lone wave gets no latency
+  // hiding from other waves while its SIMD partner runs MFMAs.
+  // chain j covers registers r with r % 4 == j: values k = sb*16 + r
+  float mx4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float m = sacc[0][j];
+#pragma unroll
+    for (int k = 4; k + 4 < NSB * 16; k += 8)
+      m = max3f(m, sacc[k / 16][(k % 16) + j], sacc[(k + 4) / 16][((k + 4) % 16) + j]);
+    m = max3f(m, m, sacc[NSB - 1][12 + j]);
+    mx4[j] = m;
+  }
+  const float mt = pair_max(max3f(max3f(mx4[0], mx4[1], mx4[2]), mx4[3], mx4[3])) * c2;
+  st.mtrue = fmaxf(st.mtrue, mt);
+  if (__any(mt > st.m2 + kSlack)) {
+    const float mnew = fmaxf(st.m2, mt);
+    const float alpha = __builtin_amdgcn_exp2f(st.m2 - mnew);
+    st.m2 = mnew;
+    st.lsum *= alpha;
+    st.lhat *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
+  }
+  const float neg_m2 = -st.m2;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, neg_m2));
+      sacc[sb][r] = e;
+      ps[r & 3] += e;
+    }
+  st.lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int cc = 0; cc < TK / 16; ++cc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[cc][i] = (__bf16)sacc[cc >> 1][8 * (cc & 1) + i];
+    if (LHAT) sum_bf16_weights(lh, pb[cc]);
+  }
+  if (LHAT) st.lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
+}
+
+// O^T += V^T P^T (eq. 6) for one tile. Chunk cc covers tile keys 16*cc ..
+// 16*cc + 15; in the B operand lane (h, n) element i is key
+// 16*cc + 8*(i/4) + 4*h + i%4 (the order of the score registers), and the
+// transposing reads give the A operand the same key order: source lane
+// s = lane % 16 of each 16-lane group reads V row 16*cc + 8*rr + 4*h + s/4 at
+// head-dim columns 32*db + 16*dh + 4*(s%4) .. +3. The V operands of a chunk
+// are read one chunk ahead of its MFMAs.
+template <int D, int TK>
+__device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], const bf16x8_t (&pb)[TK / 16], const char* vb,
+                                        int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int NCC = TK / 16;
+  constexpr int NDB = D / 32;
+  const int h = lane >> 5;
+  const int vi = (lane & 15) >> 2;
+  const int vq = lane & 3;
+  const int vdh = (lane >> 4) & 1;
+  bf16x8_t va[2][NDB];
+  auto load = [&](int cc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i16x4_t lo, hi;
+      {
+        const int row = 16 * cc + 4 * h + vi;
+        const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
+        lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
+      }
+      {
+        const int row = 16 * cc + 8 + 4 * h + vi;
+        const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
+        hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
+      }
+      va[cc & 1][db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  load(0);
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
+    if (cc + 1 < NCC) load(cc + 1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc & 1][db], pb[cc], oacc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// LDS reads at integer byte addresses.
+__device__ __forceinline__ bf16x8_t lds_b128(uint32_t a) {
+  return __builtin_bit_cast(bf16x8_t, *(const __attribute__((address_space(3))) uint4*)(uintptr_t)a);
+}
+
+__device__ __forceinline__ bf16x8_t lds_tr_pair(uint32_t lo, uint32_t hi) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(uintptr_t)lo);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(uintptr_t)hi);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The MFMA phase of the ping-pong kernel when it has both parts: O^T += V^T P^T
+// for the previous tile (V tile at LDS byte address va) and S^T = K Q^T for
+// this tile (K tile at ka), issued as one sequence of MFMAs whose LDS operands
+// are read PD MFMAs ahead. Operand layouts as in tile_pv and tile_scores.
+template <int D, int TK>
+__device__ __forceinline__ void mfma_phase_both(f32x16_t (&oacc)[D / 32], const bf16x8_t (&pb)[TK / 16],
+                                                uint32_t va, f32x16_t (&sacc)[TK / 32], uint32_t ka,
+                                                const bf16x8_t (&qf)[D / 16], int lane, float& lhat) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int NCC = TK / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NK = D / 16;
+  constexpr int NSB = TK / 32;
+  constexpr int NPV = NCC * NDB;
+  constexpr int NOPS = NPV + NK * NSB;
+  constexpr int PD = 3;
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  // V^T operands: rows 16*cc + 8*rr + 4*h + vi share the swizzle of row
+  // 4*h + vi, so block db has one base and cc, rr are immediate offsets.
+  const int vi = (lane & 15) >> 2;
+  const int vq = lane & 3;
+  const int vdh = (lane >> 4) & 1;
+  uint32_t vbase[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int row = 4 * h + vi;
+    const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
+    vbase[db] = va + opaque(row * ROWB + 16 * pc + 8 * (vq & 1));
+  }
+  // K operands: (ka + base of row 32*sb + n) ^ (32*kk); the ring slots are
+  // 16 KB aligned, so adding the slot does not disturb the XORed bits.
+  uint32_t kaddr[NSB];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) {
+    const int r = 32 * sb + n;
+    kaddr[sb] = ka + opaque(r * ROWB + 16 * (h ^ swz_k<CPR>(r)));
+  }
+  bf16x8_t buf[PD + 1];
+  auto load = [&](int i) __attribute__((always_inline)) {
+    if (i < NPV) {
+      const int cc = i / NDB, db = i % NDB;
+      buf[i % (PD + 1)] = lds_tr_pair(vbase[db] + 16 * cc * ROWB, vbase[db] + (16 * cc + 8) * ROWB);
+    } else {
+      const int kk = (i - NPV) / NSB, sb = (i - NPV) % NSB;
+      buf[i % (PD + 1)] = lds_b128(kaddr[sb] ^ (32 * kk));
+    }
+  };
+  const f32x16_t zero = {};
+  float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < PD; ++i) load(i);
+#pragma unroll
+  for (int i = 0; i < NOPS; ++i) {
+    if (i + PD < NOPS) load(i + PD);
+    if (i < NPV) {
+      const int cc = i / NDB, db = i % NDB;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[i % (PD + 1)], pb[cc], oacc[db], 0, 0, 0);
+      // the sum of the rounded weights rides in the MFMA stream: next to
+      // another wave's MFMAs the dot instruction waits for the matrix pipe
+      if (db == 0) sum_bf16_weights(lh, pb[cc]);
+    } else {
+      const int kk = (i - NPV) / NSB, sb = (i - NPV) % NSB;
+      sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[i % (PD + 1)], qf[kk], kk == 0 ? zero : sacc[sb],
+                                                         0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
+}
+
+// Everything a workgroup needs before its tile loop.
+template <int D>
+struct Setup {
+  KeyRows kr;
+  int64_t kbeg;      // first key of this split
+  int nst;           // tiles of this split
+  bool computes;     // this wave owns packed rows (wave-uniform)
+};
+
+template <int D, int TK, int NW>
+__device__ __forceinline__ Setup<D> setup(const AttnParams& p, int32_t* sidx, int wave) {
+  Setup<D> s;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;    // wave half
-  const int n = lane & 31;    // query column of this lane / operand row within a block
   const int split = blockIdx.x;
   const int hkv = blockIdx.y / p.row_chunks;
   const int rc = blockIdx.y - hkv * p.row_chunks;
@@ -152,301 +544,424 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   const int R = p.group * p.block_len;
   const int t0 = (int)((int64_t)split * p.tiles / p.splits);
   const int t1 = (int)((int64_t)(split + 1) * p.tiles / p.splits);
-  const int nst = t1 - t0;
-  const int64_t kbeg = (int64_t)t0 * TK;
+  s.nst = t1 - t0;
+  s.kbeg = (int64_t)t0 * TK;
 
-  // key sequence of this (batch, kv-head): byte pointers and row strides
-  const char* kpre = (const char*)p.keys.k_pre + 2 * (b * p.keys.kp_sb + hkv * p.keys.kp_sh);
-  const char* vpre = (const char*)p.keys.v_pre + 2 * (b * p.keys.vp_sb + hkv * p.keys.vp_sh);
-  const char* kblk = (const char*)p.keys.k_blk + 2 * (b * p.keys.kb_sb + hkv * p.keys.kb_sh);
-  const char* vblk = (const char*)p.keys.v_blk + 2 * (b * p.keys.vb_sb + hkv * p.keys.vb_sh);
-  const int64_t kp_st = 2 * p.keys.kp_st, vp_st = 2 * p.keys.vp_st;
-  const int64_t kb_st = 2 * p.keys.kb_st, vb_st = 2 * p.keys.vb_st;
-  const int64_t n_pre = p.keys.n_pre;
-  const int64_t n_all = p.keys.n_pre + p.keys.n_blk;
-  const bool indexed = p.keys.idx != nullptr;
+  KeyRows& kr = s.kr;
+  kr.kpre = (const char*)p.keys.k_pre + 2 * (b * p.keys.kp_sb + hkv * p.keys.kp_sh);
+  kr.vpre = (const char*)p.keys.v_pre + 2 * (b * p.keys.vp_sb + hkv * p.keys.vp_sh);
+  kr.kblk = (const char*)p.keys.k_blk + 2 * (b * p.keys.kb_sb + hkv * p.keys.kb_sh);
+  kr.vblk = (const char*)p.keys.v_blk + 2 * (b * p.keys.vb_sb + hkv * p.keys.vb_sh);
+  kr.kp_st = 2 * p.keys.kp_st, kr.vp_st = 2 * p.keys.vp_st;
+  kr.kb_st = 2 * p.keys.kb_st, kr.vb_st = 2 * p.keys.vb_st;
+  kr.n_pre = p.keys.n_pre;
+  kr.n_all = p.keys.n_pre + p.keys.n_blk;
+  kr.hole = p.keys.k_hole, kr.hole_len = p.keys.k_hole_len;
+  kr.indexed = p.keys.idx != nullptr;
+  kr.off32 = p.keys.off32 != 0;
 
-  // ---- retained-row indices of this split's prefix keys, staged in LDS ----
-  if (indexed) {
-    const int64_t lo = kbeg < n_pre ? kbeg : n_pre;
-    const int64_t hi0 = kbeg + (int64_t)nst * TK;
-    const int64_t hi = hi0 < n_pre ? hi0 : n_pre;
-    const int32_t* src = p.keys.idx + ((int64_t)b * p.kv_heads + hkv) * n_pre;
+  // retained-row indices of this split's prefix keys, staged in LDS
+  if (kr.indexed) {
+    const int64_t lo = s.kbeg < kr.n_pre ? s.kbeg : kr.n_pre;
+    const int64_t hi0 = s.kbeg + (int64_t)s.nst * TK;
+    const int64_t hi = hi0 < kr.n_pre ? hi0 : kr.n_pre;
+    const int32_t* src = p.keys.idx + ((int64_t)b * p.kv_heads + hkv) * kr.n_pre;
     for (int64_t j = lo + tid; j < hi; j += 64 * NW) {
       int64_t r = src[j];
       r = r < 0 ? 0 : (r >= p.keys.p_rows ? p.keys.p_rows - 1 : r);
-      sidx[j - kbeg] = (int32_t)r;
+      sidx[j - s.kbeg] = (int32_t)r;
     }
     __syncthreads();
   }
+  s.computes = wave * 32 < p.rows_per_wg && rc * p.rows_per_wg + wave * 32 < R;
+  return s;
+}
 
-  // ---- query fragment (B operand of S^T = K Q^T), resident for the loop ----
-  const int prow = rc * p.rows_per_wg + wave * 32 + n;  // packed row of this lane
-  const bool computes = wave * 32 < p.rows_per_wg && rc * p.rows_per_wg + wave * 32 < R;  // wave-uniform
-  const bool row_ok = computes && prow < R;
-  int g = 0, qi = 0;
-  if (row_ok) {
-    g = prow / p.block_len;
-    qi = prow - g * p.block_len;
+// The query row a lane owns: packed row prow = g * Bq + qi of q-head hq,
+// sequence row srow (through the row map) and its index mrow in the per-row
+// arrays. Cheap to recompute, so it is not kept alive across the tile loop.
+struct RowInfo {
+  int b, hq, g, qi;
+  int64_t srow, mrow;
+  bool row_ok;
+};
+
+__device__ __forceinline__ RowInfo row_info(const AttnParams& p, int wave, int lane) {
+  RowInfo ri;
+  const int hkv = blockIdx.y / p.row_chunks;
+  const int rc = blockIdx.y - hkv * p.row_chunks;
+  ri.b = blockIdx.z;
+  const int R = p.group * p.block_len;
+  const int prow = rc * p.rows_per_wg + wave * 32 + (lane & 31);
+  ri.row_ok = wave * 32 < p.rows_per_wg && prow < R;
+  ri.g = 0, ri.qi = 0;
+  if (ri.row_ok) {
+    ri.g = prow / p.block_len;
+    ri.qi = prow - ri.g * p.block_len;
   }
-  const int hq = hkv * p.group + g;
-  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);  // sequence row
-  const int64_t mrow = ((int64_t)b * p.q_heads + hq) * p.rows.row_pitch + srow;  // per-row arrays
-  bf16x8_t qf[D / 16];
-  {
-    const uint16_t* qrow = (const uint16_t*)p.q + b * p.q_sb + hq * p.q_sh + srow * p.q_st;
+  ri.hq = hkv * p.group + ri.g;
+  ri.srow = ri.qi + (ri.qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);
+  ri.mrow = ((int64_t)ri.b * p.q_heads + ri.hq) * p.rows.row_pitch + ri.srow;
+  return ri;
+}
+
+// Query fragment (B operand of S^T = K Q^T), resident for the loop.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const AttnParams& p, const RowInfo& s, int h) {
+  const uint16_t* qrow = (const uint16_t*)p.q + s.b * p.q_sb + s.hq * p.q_sh + s.srow * p.q_st;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok) v = *(const uint4*)(qrow + 16 * kk + 8 * h);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, v);
-    }
+  for (int kk = 0; kk < D / 16; ++kk) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (s.row_ok) v = *(const uint4*)(qrow + 16 * kk + 8 * h);
+    qf[kk] = __builtin_bit_cast(bf16x8_t, v);
   }
+}
 
-  // ---- DMA of one tile into a ring slot ----
-  // Instruction k of a stage fills 1 KB: K rows for k < INS/2, V rows after.
-  // Lane t writes LDS slot (row, physical chunk t % CPR), which holds the
-  // row's logical chunk (t % CPR) ^ swizzle(row).
-  const int lrow = lane / CPR;
-  const int lchunk = lane % CPR;
-  auto issue = [&](int t) {
-    char* slot = ring + (t % NS) * STB;
-    const int64_t key0 = kbeg + (int64_t)t * TK;
-    const bool dense = !indexed && key0 + TK <= n_pre;  // tile inside the dense prefix
+// Empty state, or the initial state from a cached partial (LaCache Appendix J:
+// the running (m, l, O~) of a later step starts from the cache): O~ = l * o,
+// m in base 2, l carried by the lanes of the first wave half.
+template <int D>
+__device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p, const RowInfo& s, int h) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int k = wave * IPW + j;   // wave-uniform
-      const bool isv = k >= INS / 2;
-      const int kk = isv ? k - INS / 2 : k;
-      const int r = kk * RPI + lrow;
-      const int lc = lchunk ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
-      const char* base = isv ? vpre : kpre;
-      int64_t st = isv ? vp_st : kp_st;
-      int64_t row = key0 + r;
-      if (dense) {
-        row += row >= p.keys.k_hole ? p.keys.k_hole_len : 0;
-      } else {
-        int64_t key = row < n_all ? row : n_all - 1;  // rows past the end: any valid row (weight 0)
-        if (key < n_pre) {
-          row = indexed ? (int64_t)sidx[key - kbeg] : key + (key >= p.keys.k_hole ? p.keys.k_hole_len : 0);
-        } else {
-          row = key - n_pre;
-          base = isv ? vblk : kblk;
-          st = isv ? vb_st : kb_st;
-        }
-      }
-      dma_1k(base + row * st + 16 * lc,
-             (uint32_t)(uintptr_t)LDS_PTR(char, slot + k * 1024));
-    }
-  };
-
-  // ---- per-lane operand coordinates of the transposing V reads ----
-  // Source lane s = lane % 16 of each 16-lane group reads V row
-  // 16*cc + 8*rr + 4*h + s/4 at head-dim columns 32*db + 16*dh + 4*(s%4) .. +3;
-  // output lane (h, m) then holds V[16*cc + 8*rr + 4*h + e][32*db + m], e = 0..3.
-  const int vi = (lane & 15) >> 2;
-  const int vq = lane & 3;
-  const int vdh = (lane >> 4) & 1;
-
-  // ---- running state ----
-  f32x16_t oacc[NDB];
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  float m2 = -INFINITY;     // reference max (base 2) shared by l and O~
-  float mtrue = -INFINITY;  // exact running max (base 2)
-  float lsum = 0.0f;        // lane-partial sum of weights
-  float lhat = 0.0f;        // lane-partial sum of the bf16-rounded weights
-  const float c2 = p.scale_log2;
-  // Initial state from a cached partial (LaCache Appendix J: the running
-  // (m, l, O~) of a later step starts from the cache): O~ = l * o, m in base 2,
-  // l carried by the lanes of the first wave half.
-  if (p.init_m != nullptr && row_ok) {
-    const float mi = p.init_m[mrow];
-    const float li = p.init_l[mrow];
+    for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.0f;
+  st.m2 = -INFINITY;
+  st.mtrue = -INFINITY;
+  st.lsum = 0.0f;
+  st.lhat = 0.0f;
+  if (p.init_m != nullptr && s.row_ok) {
+    const float mi = p.init_m[s.mrow];
+    const float li = p.init_l[s.mrow];
     if (mi > -INFINITY && li > 0.0f) {
-      m2 = mi * kLog2e;
-      mtrue = m2;
-      lsum = h == 0 ? li : 0.0f;
-      lhat = lsum;
-      const float* orow = p.init_o + mrow * D;
+      st.m2 = mi * kLog2e;
+      st.mtrue = st.m2;
+      st.lsum = h == 0 ? li : 0.0f;
+      st.lhat = st.lsum;
+      const float* orow = p.init_o + s.mrow * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const float4 v = *(const float4*)(orow + 32 * db + 8 * r4 + 4 * h);
-          oacc[db][4 * r4 + 0] = v.x * li;
-          oacc[db][4 * r4 + 1] = v.y * li;
-          oacc[db][4 * r4 + 2] = v.z * li;
-          oacc[db][4 * r4 + 3] = v.w * li;
+          st.oacc[db][4 * r4 + 0] = v.x * li;
+          st.oacc[db][4 * r4 + 1] = v.y * li;
+          st.oacc[db][4 * r4 + 2] = v.z * li;
+          st.oacc[db][4 * r4 + 3] = v.w * li;
         }
     }
   }
+}
 
-  wait_vm<0>();  // the query fragment has landed before any DMA is counted
-  const int npro = nst < NS - 1 ? nst : NS - 1;
-  for (int t = 0; t < npro; ++t) issue(t);
-
-  for (int t = 0; t < nst; ++t) {
-    const int ahead = (nst - 1 - t) < (NS - 2) ? (nst - 1 - t) : (NS - 2);
-    wait_stage<IPW, NS>(ahead);
-    tile_barrier();
-    if (t + NS - 1 < nst) issue(t + NS - 1);
-    if (!computes) continue;
-
-    const char* kb = ring + (t % NS) * STB;
-    const char* vb = kb + KBYTES;
-
-    // S^T blocks: keys 32*sb + (8*(r/4) + 4*h + r%4) x query n
-    f32x16_t sacc[NSB];
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.0f;
-      const int krow = 32 * sb + n;
-      const int ksw = swz_k<CPR>(krow);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const uint4 a = *(const uint4*)(kb + krow * ROWB + 16 * ((2 * kk + h) ^ ksw));
-        sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[kk],
-                                                           sacc[sb], 0, 0, 0);
-      }
-    }
-
-    // keys past the end of the sequence (last tile only) get no weight
-    const int64_t rem = n_all - (kbeg + (int64_t)t * TK);
-    if (rem < TK) {
-      const int nvalid = (int)rem;
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= nvalid) sacc[sb][r] = -INFINITY;
-        }
-    }
-
-    // online softmax (eqs. 2-5) in base 2 with a lazily moved reference max
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-    const float mt = pair_max(mx) * c2;
-    mtrue = fmaxf(mtrue, mt);
-    if (__any(mt > m2 + kSlack)) {
-      const float mnew = fmaxf(m2, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      m2 = mnew;
-      lsum *= alpha;
-      lhat *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    float ps = 0.0f;
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[sb][r], c2, -m2));
-        sacc[sb][r] = e;
-        ps += e;
-      }
-    lsum += ps;
-
-    // O^T += V^T P^T (eq. 6); chunk cc covers tile keys 16*cc .. 16*cc+15
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      bf16x8_t pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[cc >> 1][8 * (cc & 1) + i];
-      {
-        bf16x2_t one;
-        one[0] = (__bf16)1.0f;
-        one[1] = (__bf16)1.0f;
-        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, lhat, false);
-        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, lhat, false);
-        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, lhat, false);
-        lhat = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, lhat, false);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        i16x4_t lo, hi;
-        {
-          const int row = 16 * cc + 4 * h + vi;
-          const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
-        }
-        {
-          const int row = 16 * cc + 8 + 4 * h + vi;
-          const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
-        }
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- finish: o = O~ / l, L = m + ln l (natural-log units) ----
-  const float ltot = pair_sum(lsum);
-  const float lhtot = pair_sum(lhat);
+// Finish: o = O~ / l, L = m + ln l (natural-log units), to the final O + LSE,
+// a caller's partial, or the split workspace.
+template <int D>
+__device__ __forceinline__ void finish(const RowState<D>& st, const AttnParams& p, const RowInfo& s, int h) {
+  const float ltot = pair_sum(st.lsum);
+  const float lhtot = pair_sum(st.lhat);
   const bool live = ltot > 0.0f;
   const float inv = live ? 1.0f / lhtot : 0.0f;
-  if (!row_ok) return;
+  if (!s.row_ok) return;
   if (p.out.mode == kOutFinal) {
-    uint16_t* orow = (uint16_t*)p.out.o + b * p.out.o_sb + hq * p.out.o_sh + srow * p.out.o_st;
+    uint16_t* orow = (uint16_t*)p.out.o + s.b * p.out.o_sb + s.hq * p.out.o_sh + s.srow * p.out.o_st;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * db + 8 * r4 + 4 * h;
-        const __bf16 v0 = (__bf16)(oacc[db][4 * r4 + 0] * inv);
-        const __bf16 v1 = (__bf16)(oacc[db][4 * r4 + 1] * inv);
-        const __bf16 v2 = (__bf16)(oacc[db][4 * r4 + 2] * inv);
-        const __bf16 v3 = (__bf16)(oacc[db][4 * r4 + 3] * inv);
+        const __bf16 v0 = (__bf16)(st.oacc[db][4 * r4 + 0] * inv);
+        const __bf16 v1 = (__bf16)(st.oacc[db][4 * r4 + 1] * inv);
+        const __bf16 v2 = (__bf16)(st.oacc[db][4 * r4 + 2] * inv);
+        const __bf16 v3 = (__bf16)(st.oacc[db][4 * r4 + 3] * inv);
         uint2 w;
         w.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
         *(uint2*)(orow + d0) = w;
       }
     if (p.out.lse != nullptr && h == 0)
-      p.out.lse[mrow] = live ? (m2 + __log2f(ltot)) * kLn2 : -INFINITY;
+      p.out.lse[s.mrow] = live ? (st.m2 + __log2f(ltot)) * kLn2 : -INFINITY;
   } else {
     const int64_t base = p.out.mode == kOutSplit
-                             ? (int64_t)split * p.out.split_rows + ((int64_t)b * p.q_heads + hq) * p.block_len + qi
-                             : mrow;
+                             ? (int64_t)blockIdx.x * p.out.split_rows +
+                                   ((int64_t)s.b * p.q_heads + s.hq) * p.block_len + s.qi
+                             : s.mrow;
     float* orow = p.out.po + base * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * db + 8 * r4 + 4 * h;
-        *(float4*)(orow + d0) = make_float4(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv,
-                                            oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *(float4*)(orow + d0) = make_float4(st.oacc[db][4 * r4 + 0] * inv, st.oacc[db][4 * r4 + 1] * inv,
+                                            st.oacc[db][4 * r4 + 2] * inv, st.oacc[db][4 * r4 + 3] * inv);
       }
     if (h == 0) {
       // export the exact max: l is re-referenced from m2 to it
-      p.out.pm[base] = live ? mtrue * kLn2 : -INFINITY;
-      p.out.pl[base] = live ? ltot * __builtin_amdgcn_exp2f(m2 - mtrue) : 0.0f;
+      p.out.pm[base] = live ? st.mtrue * kLn2 : -INFINITY;
+      p.out.pl[base] = live ? ltot * __builtin_amdgcn_exp2f(st.m2 - st.mtrue) : 0.0f;
     }
   }
+}
+
+
+// Wait until at most `ahead` later stages of this wave's DMAs are in flight
+// (IPS instructions per stage).
+template <int IPS, int NS>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if (NS >= 4 && ahead >= 2) wait_vm<(NS >= 4 ? 2 : 0) * IPS>();
+  else if (NS >= 3 && ahead >= 1) wait_vm<(NS >= 3 ? 1 : 0) * IPS>();
+  else wait_vm<0>();
+}
+
+// Wait until at most n of this wave's DMA instructions are in flight
+// (n a multiple of IPW, at most 4 * IPW).
+template <int IPW>
+__device__ __forceinline__ void wait_inflight(int n) {
+  if (n >= 4 * IPW) wait_vm<(4 * IPW < 64 ? 4 * IPW : 63)>();
+  else if (n >= 3 * IPW) wait_vm<(3 * IPW < 64 ? 3 * IPW : 63)>();
+  else if (n >= 2 * IPW) wait_vm<2 * IPW>();
+  else if (n >= IPW) wait_vm<IPW>();
+  else wait_vm<0>();
+}
+
+// One to four waves (up to 128 packed rows): every wave runs scores, softmax
+// and PV of a tile in turn, the K/V tiles of a stage stored together in a ring
+// of NS stages, NS - 1 tiles in flight, one barrier per tile.
+template <int D, int NW, int TK, int NS>
+__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) {
+  constexpr int TB = TK * D * 2;           // bytes of a K (or V) tile
+  constexpr int IPW = TB / 1024 / NW;      // DMA instructions per wave per K (or V) tile
+  static_assert(IPW >= 1 && IPW * NW * 1024 == TB, "every wave issues the same number of DMAs");
+  static_assert(2 * IPW * (NS - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char ring[NS * 2 * TB];
+  __shared__ int32_t sidx[kIdxCap];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  const Setup<D> s = setup<D, TK, NW>(p, sidx, wave);
+  bf16x8_t qf[D / 16];
+  RowState<D> st;
+  {
+    const RowInfo ri = row_info(p, wave, lane);
+    load_q<D>(qf, p, ri, h);
+    init_state<D>(st, p, ri, h);
+  }
+  const uint32_t ring_lds = lds_addr(ring);
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t slot = ring_lds + (t % NS) * 2 * TB;
+    const int64_t key0 = s.kbeg + (int64_t)t * TK;
+    dma_tile<D, TK, NW>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
+    dma_tile<D, TK, NW>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
+  };
+
+  wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
+  const int nst = s.nst;
+  const int npro = nst < NS - 1 ? nst : NS - 1;
+  for (int t = 0; t < npro; ++t) issue(t);
+
+  for (int t = 0; t < nst; ++t) {
+    const int ahead = (nst - 1 - t) < (NS - 2) ? (nst - 1 - t) : (NS - 2);
+    wait_stage<2 * IPW, NS>(ahead);
+    tile_barrier();
+    if (t + NS - 1 < nst) issue(t + NS - 1);
+    if (!s.computes) continue;
+    const char* kb = ring + (t % NS) * 2 * TB;
+    f32x16_t sacc[TK / 32];
+    bf16x8_t pb[TK / 16];
+    tile_scores<D, TK>(sacc, kb, qf, n, h);
+    tile_softmax<D, TK, true>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), h);
+    tile_pv<D, TK>(st.oacc, pb, kb + TB, lane);
+  }
+  finish<D>(st, p, row_info(p, wave, opaque(lane)), h);
+}
+
+// Eight waves (129 to 256 packed rows), ping-pong. Per tile t every wave runs
+// an MFMA phase M(t) = {PV of tile t-1, scores of tile t} and a softmax phase
+// X(t). Waves 0-3 run M(t) then X(t); waves 4-7 run one phase later, so at
+// every moment each SIMD holds one wave in an MFMA phase and one in a softmax
+// phase (wave w and w+4 share a SIMD). Two barriers per tile separate the
+// phases: slot 2t holds M(t) of the leading half and X(t-1) of the lagging
+// half, slot 2t+1 X(t) of the leading half and M(t) of the lagging half.
+//
+// K and V have rings of their own. K of tile t is read in M(t) (slots 2t and
+// 2t+1), V of tile t in M(t+1) (slots 2t+2 and 2t+3); a DMA issued after the
+// barrier that opens a slot may overwrite only ring slots whose last reader
+// ran before that barrier.
+//
+// DW (dedicated DMA wave, at most 224 packed rows): wave 7 owns no rows and
+// issues every DMA; the computing waves never wait behind the memory
+// pipeline, whose queue stalls the issuing wave while it drains. One wave can
+// keep at most 63 loads (of 1 KB) in flight: K runs two tiles ahead (ring of
+// three), V three tiles ahead (ring of five, one slot still being read when
+// the next V tile is issued). Otherwise all eight waves issue their share:
+// K three tiles ahead, V two (rings of four).
+template <int D, bool DW>
+__global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
+  constexpr int NW = 8;
+  constexpr int TK = 64;
+  constexpr int NSK = DW ? 3 : 4;
+  constexpr int NSV = DW ? 5 : 4;
+  constexpr int TB = TK * D * 2;
+  constexpr int INT = TB / 1024;                // DMA instructions per K (or V) tile
+  constexpr int IPW = DW ? INT : INT / NW;      // per issuing wave
+  static_assert(IPW >= 1 && (DW || IPW * NW == INT), "every issuing wave issues the same number of DMAs");
+  static_assert((DW ? 3 : 4) * IPW < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char kring[NSK * TB];
+  __shared__ __attribute__((aligned(1024))) char vring[NSV * TB];
+  __shared__ int32_t sidx[kIdxCap];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int n = lane & 31;
+  const Setup<D> s = setup<D, TK, NW>(p, sidx, wave);
+  bf16x8_t qf[D / 16];
+  RowState<D> st;
+  {
+    const RowInfo ri = row_info(p, wave, lane);
+    load_q<D>(qf, p, ri, h);
+    init_state<D>(st, p, ri, h);
+  }
+
+  const int T = s.nst;
+  const uint32_t kring_lds = lds_addr(kring);
+  const uint32_t vring_lds = lds_addr(vring);
+  const bool issuer = !DW || wave == NW - 1;  // wave-uniform
+  const int k0 = DW ? 0 : wave * IPW;         // first instruction of this wave's share
+  // DMA schedule of the issuing waves, by slot q (negative q: before the loop).
+  // Distributed: slot 2t issues K of tile t+3, then V of tile t+2.
+  // DW: slot 2t issues K of tile t+2, slot 2t+1 V of tile t+3 (issuing V in
+  // the odd slots splits the DMA wave's issue stalls over both phases).
+  auto k_at = [&](int q) __attribute__((always_inline)) { return (q & 1) ? -1 : q / 2 + (DW ? 2 : 3); };
+  auto v_at = [&](int q) __attribute__((always_inline)) {
+    return DW ? ((q & 1) ? (q - 1) / 2 + 3 : -1) : ((q & 1) ? -1 : q / 2 + 2);
+  };
+  auto issue_tile = [&](bool isv, int tt) __attribute__((always_inline)) {
+    if (tt < 0 || tt >= T) return;
+    const int64_t key0 = s.kbeg + (int64_t)tt * TK;
+    const uint32_t dst = isv ? vring_lds + (tt % NSV) * TB : kring_lds + (tt % NSK) * TB;
+    if (DW) {
+      dma_tile_all<D, TK>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
+    } else {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) dma_one<D, TK>(s.kr, isv, key0, dst, k0 + j, lane, sidx, s.kbeg);
+    }
+  };
+  auto issue_slot = [&](int q) __attribute__((always_inline)) {
+    issue_tile(false, k_at(q));
+    issue_tile(true, v_at(q));
+  };
+  auto insts_at = [&](int q) __attribute__((always_inline)) {
+    const int a = k_at(q), b = v_at(q);
+    return IPW * ((a >= 0 && a < T ? 1 : 0) + (b >= 0 && b < T ? 1 : 0));
+  };
+  // DMAs in flight allowed at slot 2t: everything issued after K of tile t
+  // and V of tile t-1 (both issued by the end of slot 2t - QL).
+  constexpr int QL = DW ? 4 : 6;
+  auto allowed = [&](int t) __attribute__((always_inline)) {
+    int a = 0;
+    for (int q = 2 * t - QL + 1; q < 2 * t; ++q) a += insts_at(q);
+    return a;
+  };
+
+  f32x16_t sacc[TK / 32];
+  bf16x8_t pb[TK / 16];
+  // M(t): PV of tile t-1 (t >= 1) and scores of tile t (t < T). The first and
+  // last tiles are peeled out of the loops, whose bodies run the pipelined
+  // two-part form.
+  auto m_first = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    tile_scores<D, TK>(sacc, kring, qf, n, h);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto m_mid = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase_both<D, TK>(st.oacc, pb, vring_lds + ((t - 1) % NSV) * TB, sacc, kring_lds + (t % NSK) * TB, qf,
+                           lane, st.lhat);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto m_last = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    tile_pv<D, TK>(st.oacc, pb, vring + ((T - 1) % NSV) * TB, lane);
+    float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < TK / 16; ++cc) sum_bf16_weights(lh, pb[cc]);
+    st.lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto x_phase = [&](int t) __attribute__((always_inline)) {
+    tile_softmax<D, TK, false>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), h);
+  };
+
+  wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
+  if (issuer)
+    for (int q = -6; q < 0; ++q) issue_slot(q);  // every slot before 0 of either schedule
+  // Slot 2t: the issuing waves wait until K of tile t and V of tile t-1 have
+  // landed, barrier, then issue the slot's DMAs. Slot 2t+1: barrier, DMAs.
+  auto even_slot = [&](int t) __attribute__((always_inline)) {
+    if (issuer) wait_inflight<IPW>(allowed(t));
+    tile_barrier();
+    if (issuer) issue_slot(2 * t);
+  };
+  auto odd_slot = [&](int t) __attribute__((always_inline)) {
+    tile_barrier();
+    if (DW && issuer) issue_slot(2 * t + 1);
+  };
+  const bool work = s.computes && T > 0;  // wave-uniform
+  if (wave < NW / 2) {
+    // leading half: M(t) in slot 2t, X(t) in slot 2t+1
+    even_slot(0);
+    if (work) m_first();
+    odd_slot(0);
+    if (work) x_phase(0);
+    for (int t = 1; t < T; ++t) {
+      even_slot(t);
+      if (work) m_mid(t);
+      odd_slot(t);
+      if (work) x_phase(t);
+    }
+    if (T > 0) {
+      even_slot(T);
+      if (work) m_last();
+      odd_slot(T);
+    }
+  } else {
+    // lagging half: X(t-1) in slot 2t, M(t) in slot 2t+1
+    even_slot(0);
+    odd_slot(0);
+    if (work) m_first();
+    for (int t = 1; t < T; ++t) {
+      even_slot(t);
+      if (work) x_phase(t - 1);
+      odd_slot(t);
+      if (work) m_mid(t);
+    }
+    if (T > 0) {
+      even_slot(T);
+      if (work) x_phase(T - 1);
+      odd_slot(T);
+      if (work) m_last();
+    }
+  }
+  finish<D>(st, p, row_info(p, wave, opaque(lane)), h);
 }
 
 // Launch shapes: NW waves per workgroup (each 32 packed rows), TK keys per
 // tile, NS ring stages.
 template <int D, int NW>
 hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream) {
-  constexpr int TK = NW == 1 ? 32 : 64;
-  constexpr int NS = 4;
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, p);
+  if constexpr (NW == 8) {
+    if (p.rows_per_wg <= 32 * (NW - 1))
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bf16_pp_kernel<D, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    constexpr int TK = NW == 1 ? 32 : 64;
+    constexpr int NS = 4;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ the same workload.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--path full|cached]
   python bench.py --extra          # also one JSON line per secondary path
   python bench.py --copy-probe     # plain device copy of known size (counter scale)
+  python bench.py --record-traffic DIR   # write the traffic record from rocprofv3 runs
 """
 
 from __future__ import annotations
@@ -104,6 +105,77 @@ def cpu_baseline(sh: datagen.Shape, inp, budget_s: float = 10.0):
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"the whole {sh.name} workload (all {sh.batch * sh.q_heads} (batch, q-head) pairs), "
                       f"{len(times)} passes, median {t:.2f} s per pass, numpy float64"}
+
+
+KERNEL_SOURCE = "cached_block_attention_amd/csrc/attn_bf16.hip"
+
+
+def attention_kernel_name(sh: datagen.Shape) -> str:
+    """Name of the attention kernel a blkattn_full call of this workload runs:
+    eight-wave workgroups (more than 128 packed rows per kv-head chunk) run the
+    ping-pong kernel, fp32 workloads the fp32 kernel."""
+    if sh.dtype != datagen.BF16:
+        return "attn_f32_kernel"
+    rows = sh.q_heads // sh.kv_heads * sh.block_len
+    chunks = -(-rows // 256) if rows > 256 else 1
+    return "attn_bf16_pp_kernel" if -(-rows // chunks) > 128 else "attn_bf16_kernel"
+
+
+def record_traffic(top: str, out_path: str):
+    """Traffic record of the metric workload's attention kernel from four
+    rocprofv3 counter runs under `top`: pmc_fetch / pmc_write (FETCH_SIZE /
+    WRITE_SIZE of `bench.py --steps 5 --warmup 2 --no-cpu-baseline`) and
+    pmc_cfetch / pmc_cwrite (the same counters over `bench.py --copy-probe`).
+    The copy moves a known number of bytes, which gives each counter's scale."""
+    import csv
+    import glob
+    import hashlib
+
+    def per_dispatch(run, kernel):
+        files = glob.glob(os.path.join(top, run, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter CSV under {os.path.join(top, run)}")
+        vals = []
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if kernel in r.get("Kernel_Name", ""):
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"kernel {kernel!r} not found in {run}")
+        return sum(vals) / len(vals)
+
+    sh = datagen.WORKLOADS["dream_gqa"]
+    kern = attention_kernel_name(sh)
+    copy_bytes = 1024 * 1024 * 1024
+    cf = per_dispatch("pmc_cfetch", "copyBuffer")
+    cw = per_dispatch("pmc_cwrite", "copyBuffer")
+    fetch_scale = copy_bytes / (cf * 1024.0)
+    write_scale = copy_bytes / (cw * 1024.0)
+    f = per_dispatch("pmc_fetch", kern)
+    w = per_dispatch("pmc_write", kern)
+    with open(os.path.join(ROOT, KERNEL_SOURCE), "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    rec = {
+        "kernel": kern,
+        "workload": "dream_gqa: bf16 B4 Hq28/Hkv4 d128 P32768 Bq32, 16 key splits",
+        "kernel_source": KERNEL_SOURCE,
+        "kernel_source_sha256": sha,
+        "fetch_size_kib_per_dispatch": round(f, 1),
+        "write_size_kib_per_dispatch": round(w, 1),
+        "copy_probe": {"bytes": copy_bytes, "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1),
+                       "fetch_scale": fetch_scale, "write_scale": write_scale},
+        "bytes_per_launch": int(round(f * 1024.0 * fetch_scale + w * 1024.0 * write_scale)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- python3 bench.py --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- python3 bench.py --copy-probe",
+        ],
+    }
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
 
 
 def copy_probe(mib: int = 1024):
@@ -293,13 +365,17 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps first; the GPU clock needs some 300 back-to-back calls to ramp up "
+                         "from idle, so the timed steps see the steady state")
     ap.add_argument("--workload", default="dream_gqa",
                     choices=sorted(k for k, w in datagen.WORKLOADS.items() if w.block_start is None))
     ap.add_argument("--path", default="full", choices=["full", "cached"],
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write the --traffic record from the four rocprofv3 counter runs under DIR")
     ap.add_argument("--extra-path", choices=EXTRA_PATHS, action="append",
                     help="with --extra: only this secondary path (repeatable)")
     ap.add_argument("--extra", action="store_true",
@@ -310,6 +386,9 @@ def main():
                          "(used only while its kernel-source hash matches the current source)")
     args = ap.parse_args()
 
+    if args.record_traffic:
+        record_traffic(args.record_traffic, args.traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the path shards "
@@ -422,7 +501,7 @@ def main():
         "mfma_frac_step": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_bf16_kernel" if sh.dtype == datagen.BF16 else "attn_f32_kernel",
+            "kernel": attention_kernel_name(sh),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -173,14 +173,21 @@ void fill_keys(KeySeq& ks, const blkattn_dims* d, const blkattn_tensor* k_pre, c
     ks.kp_sb = k_pre->stride_b, ks.kp_sh = k_pre->stride_h, ks.kp_st = k_pre->stride_t;
     ks.v_pre = v_pre->data;
     ks.vp_sb = v_pre->stride_b, ks.vp_sh = v_pre->stride_h, ks.vp_st = v_pre->stride_t;
-    const int64_t st = (ks.kp_st > ks.vp_st ? ks.kp_st : ks.vp_st) * elt_bytes(d->dtype);
-    ks.off32 = st <= ((int64_t)1 << 25);  // 64 rows of the tile plus a row stay below 2^31 bytes
   }
   if (n_blk > 0) {
     ks.k_blk = k_blk->data;
     ks.kb_sb = k_blk->stride_b, ks.kb_sh = k_blk->stride_h, ks.kb_st = k_blk->stride_t;
     ks.v_blk = v_blk->data;
     ks.vb_sb = v_blk->stride_b, ks.vb_sh = v_blk->stride_h, ks.vb_st = v_blk->stride_t;
+  }
+  // Byte offsets inside any 64-row tile (plus the row itself) fit 31 bits, so
+  // the kernels may address a tile as a 64-bit base plus 32-bit lane offsets.
+  int64_t st = 0;
+  for (int64_t x : {ks.kp_st, ks.vp_st, ks.kb_st, ks.vb_st}) st = x > st ? x : st;
+  ks.off32 = st * elt_bytes(d->dtype) <= ((int64_t)1 << 25);
+  if (idx != nullptr) {
+    const int64_t pst = (ks.kp_st > ks.vp_st ? ks.kp_st : ks.vp_st) * elt_bytes(d->dtype);
+    ks.gather32 = ks.p_rows * pst + pst <= ((int64_t)1 << 31);
   }
 }
 

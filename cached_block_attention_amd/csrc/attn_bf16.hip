@@ -161,7 +161,7 @@ struct KeyRows {
   const char* vblk;
   int64_t kp_st, vp_st, kb_st, vb_st;  // row strides in bytes
   int64_t n_pre, n_all, hole, hole_len;
-  bool indexed, off32;
+  bool indexed, off32, gather32;
 };
 
 // A value hidden from the optimiser: what is computed from it is recomputed
@@ -185,36 +185,84 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
 // read a valid row (their weight is 0); retained-row indices come from sidx
 // (this split's, from key kbeg on). Inside the dense prefix, with 32-bit tile
 // offsets, the source is a scalar tile base plus a per-lane offset.
+// A tile whose rows all come from one strided segment: the dense prefix on
+// one side of the key hole, or the block. Rows past the segment's end (the
+// last tile of the sequence) repeat its last row; their weight is 0.
+struct SegTile {
+  const char* base;  // row 0 of the tile
+  int64_t st;        // row stride in bytes
+  int valid;         // rows inside the segment
+};
+
 template <int TK>
 __device__ __forceinline__ bool tile_is_fast(const KeyRows& kr, int64_t key0) {
-  return !kr.indexed && key0 + TK <= kr.n_pre && kr.off32 && (key0 + TK <= kr.hole || key0 >= kr.hole);
+  if (!kr.off32) return false;
+  if (key0 >= kr.n_pre) return true;  // block rows
+  return !kr.indexed && key0 + TK <= kr.n_pre && (key0 + TK <= kr.hole || key0 >= kr.hole);
+}
+
+template <int TK>
+__device__ __forceinline__ SegTile seg_tile(const KeyRows& kr, bool isv, int64_t key0) {
+  SegTile f;
+  if (key0 >= kr.n_pre) {
+    f.st = isv ? kr.vb_st : kr.kb_st;
+    f.base = (isv ? kr.vblk : kr.kblk) + (key0 - kr.n_pre) * f.st;
+    const int64_t left = kr.n_all - key0;
+    f.valid = left < TK ? (int)left : TK;
+  } else {
+    f.st = isv ? kr.vp_st : kr.kp_st;
+    f.base = (isv ? kr.vpre : kr.kpre) + (key0 + (key0 >= kr.hole ? kr.hole_len : 0)) * f.st;
+    f.valid = TK;
+  }
+  f.base = uniform_ptr(f.base);
+  return f;
 }
 
 template <int D, int TK>
-__device__ __forceinline__ void dma_one_fast(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k,
-                                             int lane) {
+__device__ __forceinline__ void dma_one_fast(const SegTile& f, bool isv, uint32_t dst, int k, int lane) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int RPI = 1024 / ROWB;
-  const int64_t row0 = key0 + (key0 >= kr.hole ? kr.hole_len : 0);
-  const int64_t st = isv ? kr.vp_st : kr.kp_st;
-  const char* sbase = uniform_ptr((isv ? kr.vpre : kr.kpre) + row0 * st);
+  const int ln = opaque(lane);
+  const int r = k * RPI + ln / CPR;
+  const int rs = r < f.valid ? r : f.valid - 1;
+  const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+  dma_1k_s(f.base, (uint32_t)rs * (uint32_t)f.st + 16 * lc, dst + k * 1024);
+}
+
+// A tile of retained (gathered) prefix rows whose byte offsets from the head's
+// first row fit 31 bits: scalar head base plus per-lane offsets from the
+// staged indices.
+template <int TK>
+__device__ __forceinline__ bool tile_is_gather(const KeyRows& kr, int64_t key0) {
+  return kr.indexed && kr.gather32 && key0 + TK <= kr.n_pre;
+}
+
+template <int D, int TK>
+__device__ __forceinline__ void dma_one_gather(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k,
+                                               int lane, const int32_t* sidx, int64_t kbeg) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPI = 1024 / ROWB;
+  const char* sbase = uniform_ptr(isv ? kr.vpre : kr.kpre);
+  const uint32_t st = (uint32_t)(isv ? kr.vp_st : kr.kp_st);
   const int ln = opaque(lane);
   const int r = k * RPI + ln / CPR;
   const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
-  dma_1k_s(sbase, (uint32_t)r * (uint32_t)st + 16 * lc, dst + k * 1024);
+  const uint32_t row = (uint32_t)sidx[key0 - kbeg + r];
+  dma_1k_s(sbase, row * st + 16 * lc, dst + k * 1024);
 }
 
+// The general form: a 64-bit address per lane, for any tile. Waves that
+// issue only a few DMAs per tile between their own compute use it everywhere:
+// the scalar-base forms above cost them more in readfirstlane and scalar
+// address work than they save.
 template <int D, int TK>
 __device__ __forceinline__ void dma_one(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k, int lane,
                                         const int32_t* sidx, int64_t kbeg) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int RPI = 1024 / ROWB;
-  if (tile_is_fast<TK>(kr, key0)) {
-    dma_one_fast<D, TK>(kr, isv, key0, dst, k, lane);
-    return;
-  }
   const bool dense = !kr.indexed && key0 + TK <= kr.n_pre;
   const int r = k * RPI + lane / CPR;
   const int lc = (lane % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
@@ -245,8 +293,14 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
                                              const int32_t* sidx, int64_t kbeg) {
   constexpr int INT = TK * D * 2 / 1024;
   if (tile_is_fast<TK>(kr, key0)) {
+    const SegTile f = seg_tile<TK>(kr, isv, key0);
 #pragma unroll
-    for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(kr, isv, key0, dst, k, lane);
+    for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(f, isv, dst, k, lane);
+    return;
+  }
+  if (tile_is_gather<TK>(kr, key0)) {
+#pragma unroll
+    for (int k = 0; k < INT; ++k) dma_one_gather<D, TK>(kr, isv, key0, dst, k, lane, sidx, kbeg);
     return;
   }
 #pragma unroll 1
@@ -254,7 +308,7 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
 }
 
 // This wave's share of the DMA of one K (or V) tile: with NW waves issuing,
-// wave w issues instructions w*IPW .. w*IPW + IPW - 1.
+// wave w issues instructions w*IPW .. w*IPW + IPW - 1, in the general form.
 template <int D, int TK, int NW>
 __device__ __forceinline__ void dma_tile(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int wave,
                                          int lane, const int32_t* sidx, int64_t kbeg) {
@@ -264,46 +318,24 @@ __device__ __forceinline__ void dma_tile(const KeyRows& kr, bool isv, int64_t ke
 }
 
 // S^T = K Q^T for one tile: sacc[sb] holds keys 32*sb + 8*(r/4) + 4*h + r%4
-// (register r) against this lane's query. The K operands are read from LDS
-// two head-dim steps ahead of their MFMAs; the scheduling barriers keep the
-// compiler from hoisting every read of the tile (which would need 64 more
-// registers).
+// (register r) against this lane's query. Scheduling is left to the compiler,
+// which interleaves these MFMAs with the vector work around them.
 template <int D, int TK>
 __device__ __forceinline__ void tile_scores(f32x16_t (&sacc)[TK / 32], const char* kb,
                                             const bf16x8_t (&qf)[D / 16], int n, int h) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
-  constexpr int NSB = TK / 32;
-  constexpr int NK = D / 16;
-  constexpr int PF = 1;
-  // Row r = 32*sb + n at logical chunk 2*kk + h sits at byte
-  // r*ROWB + 16*((2*kk + h) ^ swz(r)) = (r*ROWB + 16*(h ^ swz(r))) ^ (32*kk):
-  // the chunk bits lie below the row bits, so one XOR per step.
-  int kbase[NSB];
 #pragma unroll
-  for (int sb = 0; sb < NSB; ++sb) {
-    const int r = 32 * sb + n;
-    kbase[sb] = opaque(r * ROWB + 16 * (h ^ swz_k<CPR>(r)));
-  }
-  uint4 ka[PF + 1][NSB];
-  auto load = [&](int kk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) ka[kk % (PF + 1)][sb] = *(const uint4*)(kb + (kbase[sb] ^ (32 * kk)));
-  };
-#pragma unroll
-  for (int sb = 0; sb < NSB; ++sb)
+  for (int sb = 0; sb < TK / 32; ++sb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[sb][r] = 0.0f;
+    const int krow = 32 * sb + n;
+    const int ksw = swz_k<CPR>(krow);
 #pragma unroll
-  for (int kk = 0; kk < PF && kk < NK; ++kk) load(kk);
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    if (kk + PF < NK) load(kk + PF);
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-      sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[kk % (PF + 1)][sb]),
-                                                         qf[kk], sacc[sb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const uint4 a = *(const uint4*)(kb + krow * ROWB + 16 * ((2 * kk + h) ^ ksw));
+      sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qf[kk], sacc[sb], 0, 0, 0);
+    }
   }
 }
 
@@ -399,23 +431,20 @@ __device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t
 // 16*cc + 8*(i/4) + 4*h + i%4 (the order of the score registers), and the
 // transposing reads give the A operand the same key order: source lane
 // s = lane % 16 of each 16-lane group reads V row 16*cc + 8*rr + 4*h + s/4 at
-// head-dim columns 32*db + 16*dh + 4*(s%4) .. +3. The V operands of a chunk
-// are read one chunk ahead of its MFMAs.
+// head-dim columns 32*db + 16*dh + 4*(s%4) .. +3.
 template <int D, int TK>
 __device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], const bf16x8_t (&pb)[TK / 16], const char* vb,
                                         int lane) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
-  constexpr int NCC = TK / 16;
-  constexpr int NDB = D / 32;
   const int h = lane >> 5;
   const int vi = (lane & 15) >> 2;
   const int vq = lane & 3;
   const int vdh = (lane >> 4) & 1;
-  bf16x8_t va[2][NDB];
-  auto load = [&](int cc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int cc = 0; cc < TK / 16; ++cc)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
       i16x4_t lo, hi;
       {
         const int row = 16 * cc + 4 * h + vi;
@@ -427,18 +456,9 @@ __device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], const bf16x8_t
         const int pc = (4 * db + 2 * vdh + (vq >> 1)) ^ swz_v<CPR>(row);
         hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4_t, vb + row * ROWB + 16 * pc + 8 * (vq & 1)));
       }
-      va[cc & 1][db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[db], 0, 0, 0);
     }
-  };
-  load(0);
-#pragma unroll
-  for (int cc = 0; cc < NCC; ++cc) {
-    if (cc + 1 < NCC) load(cc + 1);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc & 1][db], pb[cc], oacc[db], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 // LDS reads at integer byte addresses.
@@ -559,6 +579,7 @@ __device__ __forceinline__ Setup<D> setup(const AttnParams& p, int32_t* sidx, in
   kr.hole = p.keys.k_hole, kr.hole_len = p.keys.k_hole_len;
   kr.indexed = p.keys.idx != nullptr;
   kr.off32 = p.keys.off32 != 0;
+  kr.gather32 = p.keys.gather32 != 0;
 
   // retained-row indices of this split's prefix keys, staged in LDS
   if (kr.indexed) {
@@ -952,11 +973,8 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
 template <int D, int NW>
 hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream) {
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
-  if constexpr (NW == 8) {
-    if (p.rows_per_wg <= 32 * (NW - 1))
-      hipLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_bf16_pp_kernel<D, false>), grid, dim3(512), 0, stream, p);
+  if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
+    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, p);
   } else {
     constexpr int TK = NW == 1 ? 32 : 64;
     constexpr int NS = 4;

@@ -23,7 +23,8 @@ struct KeySeq {
   // Dense prefix key j reads row j + (j >= k_hole ? k_hole_len : 0): a prefix
   // that skips the rows of a block sitting inside the sequence.
   int64_t k_hole, k_hole_len;
-  int32_t off32;                // byte offsets within any 64-row prefix tile fit 32 bits
+  int32_t off32;                // byte offsets within any 64-row tile (prefix or block) fit 31 bits
+  int32_t gather32;             // with idx: byte offsets of every prefix row (p_rows of them) fit 31 bits
   const void* k_blk;
   const void* v_blk;
   int64_t kb_sb, kb_sh, kb_st;

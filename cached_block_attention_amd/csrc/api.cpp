@@ -214,10 +214,11 @@ AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Pla
 }
 
 int launch_attn(const blkattn_dims* d, const AttnParams& p, const Plan& pl, hipStream_t stream) {
-  if (g_ev_start) hipEventRecord((hipEvent_t)g_ev_start, stream);
-  hipError_t e = d->dtype == BLKATTN_F32 ? launch_attn_f32(p, stream) : launch_attn_bf16(p, pl.waves, stream);
-  if (g_ev_stop) hipEventRecord((hipEvent_t)g_ev_stop, stream);
+  KernelEvents ev;
+  ev.start = (hipEvent_t)g_ev_start;
+  ev.stop = (hipEvent_t)g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
+  hipError_t e = d->dtype == BLKATTN_F32 ? launch_attn_f32(p, stream, ev) : launch_attn_bf16(p, pl.waves, stream, ev);
   if (e != hipSuccess) return fail(BLKATTN_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
   return BLKATTN_OK;
 }

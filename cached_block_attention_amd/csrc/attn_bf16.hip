@@ -733,15 +733,18 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   else wait_vm<0>();
 }
 
-// Wait until at most n of this wave's DMA instructions are in flight
-// (n a multiple of IPW, at most 4 * IPW).
-template <int IPW>
-__device__ __forceinline__ void wait_inflight(int n) {
-  if (n >= 4 * IPW) wait_vm<(4 * IPW < 64 ? 4 * IPW : 63)>();
-  else if (n >= 3 * IPW) wait_vm<(3 * IPW < 64 ? 3 * IPW : 63)>();
-  else if (n >= 2 * IPW) wait_vm<2 * IPW>();
-  else if (n >= IPW) wait_vm<IPW>();
-  else wait_vm<0>();
+// Wait until at most n (wave-uniform) of this wave's loads are in flight,
+// n rounded down to the nearest of the counts N, Rest... (descending, ending
+// with 0): waiting for fewer in flight than allowed is always safe.
+template <int N, int... Rest>
+__device__ __forceinline__ void wait_at_most(int n) {
+  if constexpr (sizeof...(Rest) == 0) {
+    static_assert(N == 0, "the last count is 0");
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N>();
+    else wait_at_most<Rest...>(n);
+  }
 }
 
 // One to four waves (up to 128 packed rows): every wave runs scores, softmax
@@ -797,7 +800,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   finish<D>(st, p, row_info(p, wave, opaque(lane)), h);
 }
 
-// Eight waves (129 to 256 packed rows), ping-pong. Per tile t every wave runs
+// Eight waves (at most 224 packed rows), ping-pong. Per tile t every wave runs
 // an MFMA phase M(t) = {PV of tile t-1, scores of tile t} and a softmax phase
 // X(t). Waves 0-3 run M(t) then X(t); waves 4-7 run one phase later, so at
 // every moment each SIMD holds one wave in an MFMA phase and one in a softmax
@@ -810,24 +813,25 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
 // barrier that opens a slot may overwrite only ring slots whose last reader
 // ran before that barrier.
 //
-// DW (dedicated DMA wave, at most 224 packed rows): wave 7 owns no rows and
-// issues every DMA; the computing waves never wait behind the memory
-// pipeline, whose queue stalls the issuing wave while it drains. One wave can
-// keep at most 63 loads (of 1 KB) in flight: K runs two tiles ahead (ring of
-// three), V three tiles ahead (ring of five, one slot still being read when
-// the next V tile is issued). Otherwise all eight waves issue their share:
-// K three tiles ahead, V two (rings of four).
-template <int D, bool DW>
+// Two waves issue the DMAs, each with its own vmcnt budget (one wave can
+// keep at most 63 loads of 1 KB in flight): wave 7, which owns no rows,
+// issues K, three tiles ahead (ring of four); wave 6 if it owns no rows, else
+// wave 3 (which shares its SIMD with wave 7 and so has time to spare), issues
+// V, three tiles ahead (ring of five: when V of tile t+3 is issued, V of
+// tile t-1 is still being read). Both issue right after a barrier and wait
+// for their tiles to land just before one, so that no computing wave waits
+// behind the memory pipeline in the middle of a phase.
+template <int D>
 __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   constexpr int NW = 8;
   constexpr int TK = 64;
-  constexpr int NSK = DW ? 3 : 4;
-  constexpr int NSV = DW ? 5 : 4;
+  constexpr int NSK = 4;
+  constexpr int NSV = 5;
+  constexpr int KA = NSK - 1;  // K tiles in flight ahead of the one being read
+  constexpr int VA = NSV - 2;  // V tiles issued ahead
   constexpr int TB = TK * D * 2;
-  constexpr int INT = TB / 1024;                // DMA instructions per K (or V) tile
-  constexpr int IPW = DW ? INT : INT / NW;      // per issuing wave
-  static_assert(IPW >= 1 && (DW || IPW * NW == INT), "every issuing wave issues the same number of DMAs");
-  static_assert((DW ? 3 : 4) * IPW < 64, "vmcnt range");
+  constexpr int IPW = TB / 1024;  // DMA instructions per K (or V) tile
+  static_assert(KA * IPW < 64 && VA * IPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char kring[NSK * TB];
   __shared__ __attribute__((aligned(1024))) char vring[NSV * TB];
   __shared__ int32_t sidx[kIdxCap];
@@ -848,42 +852,20 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   const int T = s.nst;
   const uint32_t kring_lds = lds_addr(kring);
   const uint32_t vring_lds = lds_addr(vring);
-  const bool issuer = !DW || wave == NW - 1;  // wave-uniform
-  const int k0 = DW ? 0 : wave * IPW;         // first instruction of this wave's share
-  // DMA schedule of the issuing waves, by slot q (negative q: before the loop).
-  // Distributed: slot 2t issues K of tile t+3, then V of tile t+2.
-  // DW: slot 2t issues K of tile t+2, slot 2t+1 V of tile t+3 (issuing V in
-  // the odd slots splits the DMA wave's issue stalls over both phases).
-  auto k_at = [&](int q) __attribute__((always_inline)) { return (q & 1) ? -1 : q / 2 + (DW ? 2 : 3); };
-  auto v_at = [&](int q) __attribute__((always_inline)) {
-    return DW ? ((q & 1) ? (q - 1) / 2 + 3 : -1) : ((q & 1) ? -1 : q / 2 + 2);
-  };
+  const bool k_issuer = wave == NW - 1;                                   // wave-uniform
+  const bool v_issuer = wave == (p.rows_per_wg <= 32 * (NW - 2) ? NW - 2 : NW / 2 - 1);
+  auto in_range = [&](int tt) __attribute__((always_inline)) { return tt >= 0 && tt < T; };
   auto issue_tile = [&](bool isv, int tt) __attribute__((always_inline)) {
-    if (tt < 0 || tt >= T) return;
+    if (!in_range(tt)) return;
     const int64_t key0 = s.kbeg + (int64_t)tt * TK;
     const uint32_t dst = isv ? vring_lds + (tt % NSV) * TB : kring_lds + (tt % NSK) * TB;
-    if (DW) {
-      dma_tile_all<D, TK>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
-    } else {
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) dma_one<D, TK>(s.kr, isv, key0, dst, k0 + j, lane, sidx, s.kbeg);
-    }
+    dma_tile_all<D, TK>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
   };
-  auto issue_slot = [&](int q) __attribute__((always_inline)) {
-    issue_tile(false, k_at(q));
-    issue_tile(true, v_at(q));
-  };
-  auto insts_at = [&](int q) __attribute__((always_inline)) {
-    const int a = k_at(q), b = v_at(q);
-    return IPW * ((a >= 0 && a < T ? 1 : 0) + (b >= 0 && b < T ? 1 : 0));
-  };
-  // DMAs in flight allowed at slot 2t: everything issued after K of tile t
-  // and V of tile t-1 (both issued by the end of slot 2t - QL).
-  constexpr int QL = DW ? 4 : 6;
-  auto allowed = [&](int t) __attribute__((always_inline)) {
-    int a = 0;
-    for (int q = 2 * t - QL + 1; q < 2 * t; ++q) a += insts_at(q);
-    return a;
+  // Tiles of [a, b] that exist, times the DMAs per tile.
+  auto insts = [&](int a, int b) __attribute__((always_inline)) {
+    const int lo = a > 0 ? a : 0;
+    const int hi = b < T - 1 ? b : T - 1;
+    return hi >= lo ? (hi - lo + 1) * IPW : 0;
   };
 
   f32x16_t sacc[TK / 32];
@@ -916,18 +898,23 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   };
 
   wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
-  if (issuer)
-    for (int q = -6; q < 0; ++q) issue_slot(q);  // every slot before 0 of either schedule
-  // Slot 2t: the issuing waves wait until K of tile t and V of tile t-1 have
-  // landed, barrier, then issue the slot's DMAs. Slot 2t+1: barrier, DMAs.
+  if (k_issuer)
+    for (int tt = 0; tt < KA; ++tt) issue_tile(false, tt);
+  if (v_issuer)
+    for (int tt = 0; tt < VA; ++tt) issue_tile(true, tt);
+  // Slot 2t opens with M(t) of the leading half, which reads K of tile t and
+  // V of tile t-1: their issuers wait until those have landed (every later
+  // DMA of theirs may still be in flight), barrier, then K of tile t+KA is
+  // issued. Slot 2t+1: barrier, then V of tile t+VA.
   auto even_slot = [&](int t) __attribute__((always_inline)) {
-    if (issuer) wait_inflight<IPW>(allowed(t));
+    if (k_issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(insts(t + 1, t + KA - 1));
+    if (v_issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(insts(t, t + VA - 1));
     tile_barrier();
-    if (issuer) issue_slot(2 * t);
+    if (k_issuer) issue_tile(false, t + KA);
   };
   auto odd_slot = [&](int t) __attribute__((always_inline)) {
     tile_barrier();
-    if (DW && issuer) issue_slot(2 * t + 1);
+    if (v_issuer) issue_tile(true, t + VA);
   };
   const bool work = s.computes && T > 0;  // wave-uniform
   if (wave < NW / 2) {
@@ -971,25 +958,26 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
 // Launch shapes: NW waves per workgroup (each 32 packed rows), TK keys per
 // tile, NS ring stages.
 template <int D, int NW>
-hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev) {
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
   if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
-    hipLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, p);
+    hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else {
     constexpr int TK = NW == 1 ? 32 : 64;
     constexpr int NS = 4;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, p);
+    hipExtLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, ev.start, ev.stop, 0,
+                          p);
   }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnParams& p, int waves, hipStream_t stream) {
+hipError_t launch_d(const AttnParams& p, int waves, hipStream_t stream, KernelEvents ev) {
   switch (waves) {
-    case 1: return launch_d_nw<D, 1>(p, stream);
-    case 2: return launch_d_nw<D, 2>(p, stream);
-    case 4: return launch_d_nw<D, 4>(p, stream);
-    case 8: return launch_d_nw<D, 8>(p, stream);
+    case 1: return launch_d_nw<D, 1>(p, stream, ev);
+    case 2: return launch_d_nw<D, 2>(p, stream, ev);
+    case 4: return launch_d_nw<D, 4>(p, stream, ev);
+    case 8: return launch_d_nw<D, 8>(p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1009,9 +997,9 @@ int bf16_workgroups_per_cu(int waves) { return waves >= 4 ? 1 : 2; }
 
 int bf16_index_cap() { return kIdxCap; }
 
-hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream) {
-  if (p.head_dim == 128) return launch_d<128>(p, waves, stream);
-  if (p.head_dim == 64) return launch_d<64>(p, waves, stream);
+hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream, KernelEvents ev) {
+  if (p.head_dim == 128) return launch_d<128>(p, waves, stream, ev);
+  if (p.head_dim == 64) return launch_d<64>(p, waves, stream, ev);
   return hipErrorInvalidValue;
 }
 

@@ -137,12 +137,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream, KernelEvents ev) {
   dim3 grid(p.splits, p.q_heads, p.batch);
   if (p.head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+    hipExtLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, p);
   else if (p.head_dim == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, p);
+    hipExtLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, stream, ev.start, ev.stop, 0, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace blkattn {
@@ -131,9 +132,18 @@ struct MassParams {
   int32_t accumulate;           // bf16: add onto mass (passes after the first)
 };
 
+// Optional timing events of one attention launch: the dispatch itself stamps
+// them with its begin and end (hipExtLaunchKernel), so their elapsed time is
+// the kernel's own duration, without the gaps that separate event records put
+// around it.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Kernel launchers (return the hipError_t of the launch).
-hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream);
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams& p, int waves, hipStream_t stream, KernelEvents ev = {});
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream, KernelEvents ev = {});
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_fill_empty(float* o, float* m, float* l, int64_t rows, int head_dim,

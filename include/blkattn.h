@@ -303,9 +303,11 @@ int blkattn_plan_splits(const blkattn_dims* dims, int op);
 
 /*
  * Measurement hook: the next blkattn_full or blkattn_prefix_partial call made
- * by this thread records `start` on its stream just before launching the
- * attention (partial) kernel and `stop` just after it, then forgets both.
- * Events are hipEvent_t handles owned by the caller. Pass NULL, NULL to clear.
+ * by this thread hands `start` and `stop` to the launch of its attention
+ * (partial) kernel, whose dispatch stamps them with the kernel's own begin and
+ * end (hipExtLaunchKernel), then forgets both; hipEventElapsedTime(start,
+ * stop) is that kernel's duration. Events are hipEvent_t handles created and
+ * owned by the caller. Pass NULL, NULL to clear.
  */
 void blkattn_set_kernel_events(void* start, void* stop);
 

@@ -76,6 +76,9 @@ def test_full_tiny_f32(ba, splits):
     dict(batch=1, q_heads=1, kv_heads=1, prefix_len=70, block_len=1),       # one query
     dict(batch=1, q_heads=40, kv_heads=5, prefix_len=130, block_len=32),    # 8 waves
     dict(batch=1, q_heads=3, kv_heads=1, prefix_len=64, block_len=32),      # 3 waves, exact tiles
+    dict(batch=1, q_heads=10, kv_heads=2, prefix_len=1000, block_len=32),   # 160 rows: waves 5, 6 idle
+    dict(batch=2, q_heads=12, kv_heads=2, prefix_len=300, block_len=32),    # 192 rows: wave 6 idle
+    dict(batch=1, q_heads=10, kv_heads=2, prefix_len=700, block_len=40),    # 200 rows: wave 6 part full
 ], ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
 @pytest.mark.parametrize("splits", [0, 1, 2, 5])
 def test_full_bf16_shapes(ba, kw, splits):

@@ -747,14 +747,18 @@ __device__ __forceinline__ void wait_at_most(int n) {
   }
 }
 
-// One to four waves (up to 128 packed rows): every wave runs scores, softmax
-// and PV of a tile in turn, the K/V tiles of a stage stored together in a ring
-// of NS stages, NS - 1 tiles in flight, one barrier per tile.
-template <int D, int NW, int TK, int NS>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) {
-  constexpr int TB = TK * D * 2;           // bytes of a K (or V) tile
-  constexpr int IPW = TB / 1024 / NW;      // DMA instructions per wave per K (or V) tile
-  static_assert(IPW >= 1 && IPW * NW * 1024 == TB, "every wave issues the same number of DMAs");
+// One to four row waves (up to 128 packed rows), or eight (225 to 256 rows):
+// every wave runs scores, softmax and PV of a tile in turn, the K/V tiles of a
+// stage stored together in a ring of NS stages, NS - 1 tiles in flight, one
+// barrier per tile. The row waves issue the DMAs, each its share of every
+// tile; with DMAW one more wave (wave NW, no rows) issues them all instead, so
+// that a row wave never stalls behind the memory pipeline between its
+// products.
+template <int D, int NW, int TK, int NS, bool DMAW = false>
+__global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnParams p) {
+  constexpr int TB = TK * D * 2;                       // bytes of a K (or V) tile
+  constexpr int IPW = DMAW ? TB / 1024 : TB / 1024 / NW;  // DMA instructions per issuing wave per K (or V) tile
+  static_assert(IPW >= 1 && (DMAW || IPW * NW * 1024 == TB), "every wave issues the same number of DMAs");
   static_assert(2 * IPW * (NS - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char ring[NS * 2 * TB];
   __shared__ int32_t sidx[kIdxCap];
@@ -763,7 +767,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int n = lane & 31;
-  const Setup<D> s = setup<D, TK, NW>(p, sidx, wave);
+  const Setup<D> s = setup<D, TK, NW + DMAW>(p, sidx, wave);
   bf16x8_t qf[D / 16];
   RowState<D> st;
   {
@@ -772,23 +776,30 @@ __global__ __launch_bounds__(64 * NW) void attn_bf16_kernel(const AttnParams p) 
     init_state<D>(st, p, ri, h);
   }
   const uint32_t ring_lds = lds_addr(ring);
+  const bool issuer = !DMAW || wave == NW;  // wave-uniform
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t slot = ring_lds + (t % NS) * 2 * TB;
     const int64_t key0 = s.kbeg + (int64_t)t * TK;
-    dma_tile<D, TK, NW>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
-    dma_tile<D, TK, NW>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
+    if (DMAW) {
+      dma_tile_all<D, TK>(s.kr, false, key0, slot, lane, sidx, s.kbeg);
+      dma_tile_all<D, TK>(s.kr, true, key0, slot + TB, lane, sidx, s.kbeg);
+    } else {
+      dma_tile<D, TK, NW>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
+      dma_tile<D, TK, NW>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
+    }
   };
 
   wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
   const int nst = s.nst;
   const int npro = nst < NS - 1 ? nst : NS - 1;
-  for (int t = 0; t < npro; ++t) issue(t);
+  if (issuer)
+    for (int t = 0; t < npro; ++t) issue(t);
 
   for (int t = 0; t < nst; ++t) {
     const int ahead = (nst - 1 - t) < (NS - 2) ? (nst - 1 - t) : (NS - 2);
-    wait_stage<2 * IPW, NS>(ahead);
+    if (issuer) wait_stage<2 * IPW, NS>(ahead);
     tile_barrier();
-    if (t + NS - 1 < nst) issue(t + NS - 1);
+    if (issuer && t + NS - 1 < nst) issue(t + NS - 1);
     if (!s.computes) continue;
     const char* kb = ring + (t % NS) * 2 * TB;
     f32x16_t sacc[TK / 32];
@@ -962,6 +973,10 @@ hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev)
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
   if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
     hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+  } else if (NW == 1 && p.tiles >= 4 * p.splits) {
+    // one row wave over a long key range: a second wave issues the DMAs
+    hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
+                          p);
   } else {
     constexpr int TK = NW == 1 ? 32 : 64;
     constexpr int NS = 4;

@@ -64,19 +64,27 @@ def algorithmic(sh: datagen.Shape, with_block: bool = True):
 def measured_traffic(path, sh: datagen.Shape, fn_path: str):
     """HBM bytes per attention-kernel launch from the committed counter record
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the record
-    is for another workload or the kernel source changed since it was taken."""
-    import hashlib
+    is for another workload or the kernel sources changed since it was taken."""
     if not path or not os.path.exists(path) or sh.name != "dream_gqa" or fn_path != "full":
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec.get("kernel_source", ""))
-    if not os.path.exists(src):
+    srcs = rec.get("kernel_sources", [])
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, x)) for x in srcs):
         return None
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec.get("kernel_source_sha256"):
-            return None
+    if sources_sha256(srcs) != rec.get("kernel_sources_sha256"):
+        return None
     return rec.get("bytes_per_launch")
+
+
+def sources_sha256(paths) -> str:
+    """SHA-256 over the concatenated contents of the given repository files."""
+    import hashlib
+    h = hashlib.sha256()
+    for x in paths:
+        with open(os.path.join(ROOT, x), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def up(x, torch):
@@ -107,7 +115,8 @@ def cpu_baseline(sh: datagen.Shape, inp, budget_s: float = 10.0):
                       f"{len(times)} passes, median {t:.2f} s per pass, numpy float64"}
 
 
-KERNEL_SOURCE = "cached_block_attention_amd/csrc/attn_bf16.hip"
+KERNEL_SOURCES = ("cached_block_attention_amd/csrc/attn_bf16.hip", "cached_block_attention_amd/csrc/gfx950.h",
+                  "cached_block_attention_amd/csrc/launch.h")
 
 
 def attention_kernel_name(sh: datagen.Shape) -> str:
@@ -131,7 +140,6 @@ def record_traffic(top: str, out_path: str):
     The copy moves a known number of bytes, which gives each counter's scale."""
     import csv
     import glob
-    import hashlib
 
     def per_dispatch(run, kernel):
         files = glob.glob(os.path.join(top, run, "**", "*counter_collection.csv"), recursive=True)
@@ -155,13 +163,11 @@ def record_traffic(top: str, out_path: str):
     write_scale = copy_bytes / (cw * 1024.0)
     f = per_dispatch("pmc_fetch", kern)
     w = per_dispatch("pmc_write", kern)
-    with open(os.path.join(ROOT, KERNEL_SOURCE), "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
     rec = {
         "kernel": kern,
         "workload": "dream_gqa: bf16 B4 Hq28/Hkv4 d128 P32768 Bq32, 16 key splits",
-        "kernel_source": KERNEL_SOURCE,
-        "kernel_source_sha256": sha,
+        "kernel_sources": list(KERNEL_SOURCES),
+        "kernel_sources_sha256": sources_sha256(KERNEL_SOURCES),
         "fetch_size_kib_per_dispatch": round(f, 1),
         "write_size_kib_per_dispatch": round(w, 1),
         "copy_probe": {"bytes": copy_bytes, "fetch_size_kib": round(cf, 1), "write_size_kib": round(cw, 1),

@@ -45,6 +45,7 @@
 //    a tile (PV of the previous tile, then the scores of this one) the other
 //    runs the softmax of its tile on the vector ALU. The matrix cores and the
 //    vector ALU of a SIMD then work at the same time instead of in turn.
+#include "gfx950.h"
 #include "launch.h"
 
 #include <math.h>
@@ -61,7 +62,6 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kSlack = 8.0f;  // log2 of the largest unnormalised weight allowed
 
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // XOR swizzle of the 16-byte chunk index of K row r (CPR chunks per row):
 // 16 consecutive rows read at one logical chunk land on distinct banks.
@@ -96,60 +96,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt vmcnt(n) leaving the other counters free (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would drain every outstanding DMA (vmcnt(0)) at each tile. LDS data is
-// ordered explicitly instead: DMA completion by s_waitcnt vmcnt before the
-// barrier, and every LDS read of a tile is consumed by an MFMA before the
-// barrier that lets its slot be refilled. The scheduling barriers keep the
-// compiler from moving any instruction across it.
-__device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// One direct-to-LDS DMA: 64 lanes x 16 bytes from per-lane global addresses
-// into 1 KB of LDS at lds_addr (wave-uniform, through M0). Written as inline
-// asm so that the compiler does not see an LDS write in flight and drain the
-// whole DMA ring (vmcnt(0)) before every LDS read; completion is ordered
-// explicitly by vmcnt waits before the tile barriers. The instruction has no
-// register results.
-__device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
-  __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
-      : "memory", "m0");
-}
-
-// The same DMA from a wave-uniform base in scalar registers plus a per-lane
-// unsigned 32-bit byte offset.
-__device__ __forceinline__ void dma_1k_s(const char* sbase, uint32_t voff, uint32_t lds_addr) {
-  __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
-      : "memory", "m0");
-}
-
-// A wave-uniform pointer moved to scalar registers.
-__device__ __forceinline__ const char* uniform_ptr(const char* q) {
-  const uint64_t v = (uint64_t)(uintptr_t)q;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
 
 constexpr int kIdxCap = 2048;  // retained-row indices staged per split
 
@@ -164,27 +110,6 @@ struct KeyRows {
   bool indexed, off32, gather32;
 };
 
-// A value hidden from the optimiser: what is computed from it is recomputed
-// where it is used instead of being hoisted out of the tile loop and kept in
-// registers (or spilled) through it.
-__device__ __forceinline__ int opaque(int x) {
-  __asm__ __volatile__("" : "+v"(x));
-  return x;
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
-  return (uint32_t)(uintptr_t)LDS_PTR(const char, ptr);
-}
-
-// DMA instruction k of the K (isv = false) or V rows of one TK-key tile
-// starting at key key0, into the LDS tile at byte address dst (TK * 2D bytes,
-// TK*2D/1024 instructions of 1 KB). Instruction k covers tile rows
-// k*RPI .. k*RPI + RPI - 1; lane t fills LDS chunk t % CPR of its row with
-// logical chunk (t % CPR) ^ swizzle(row). Keys past the end of the sequence
-// read a valid row (their weight is 0); retained-row indices come from sidx
-// (this split's, from key kbeg on). Inside the dense prefix, with 32-bit tile
-// offsets, the source is a scalar tile base plus a per-lane offset.
 // A tile whose rows all come from one strided segment: the dense prefix on
 // one side of the key hole, or the block. Rows past the segment's end (the
 // last tile of the sequence) repeat its last row; their weight is 0.
@@ -253,6 +178,14 @@ __device__ __forceinline__ void dma_one_gather(const KeyRows& kr, bool isv, int6
   dma_1k_s(sbase, row * st + 16 * lc, dst + k * 1024);
 }
 
+// DMA instruction k of the K (isv = false) or V rows of one TK-key tile
+// starting at key key0, into the LDS tile at byte address dst (TK * 2D bytes,
+// TK*2D/1024 instructions of 1 KB). Instruction k covers tile rows
+// k*RPI .. k*RPI + RPI - 1; lane t fills LDS chunk t % CPR of its row with
+// logical chunk (t % CPR) ^ swizzle(row). Keys past the end of the sequence
+// read a valid row (their weight is 0); retained-row indices come from sidx
+// (this split's, from key kbeg on).
+//
 // The general form: a 64-bit address per lane, for any tile. Waves that
 // issue only a few DMAs per tile between their own compute use it everywhere:
 // the scalar-base forms above cost them more in readfirstlane and scalar
@@ -733,19 +666,6 @@ __device__ __forceinline__ void wait_stage(int ahead) {
   else wait_vm<0>();
 }
 
-// Wait until at most n (wave-uniform) of this wave's loads are in flight,
-// n rounded down to the nearest of the counts N, Rest... (descending, ending
-// with 0): waiting for fewer in flight than allowed is always safe.
-template <int N, int... Rest>
-__device__ __forceinline__ void wait_at_most(int n) {
-  if constexpr (sizeof...(Rest) == 0) {
-    static_assert(N == 0, "the last count is 0");
-    wait_vm<0>();
-  } else {
-    if (n >= N) wait_vm<N>();
-    else wait_at_most<Rest...>(n);
-  }
-}
 
 // One to four row waves (up to 128 packed rows), or eight (225 to 256 rows):
 // every wave runs scores, softmax and PV of a tile in turn, the K/V tiles of a

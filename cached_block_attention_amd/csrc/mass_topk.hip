@@ -24,6 +24,7 @@
 // radix select over the fp32 bit patterns (non-negative floats order like
 // their bits) finds the n_keep-th largest value T, then an ordered compaction
 // takes every key above T and the lowest-indexed keys equal to T.
+#include "gfx950.h"
 #include "launch.h"
 
 #include <math.h>
@@ -51,37 +52,52 @@ __device__ __forceinline__ int mswz(int r) {
 // column: its 16 accumulator registers are 16 of the block's rows, and the
 // column sum is an in-register sum plus one exchange between the wave halves.
 // Each K fragment read from LDS feeds every row block of the wave.
+//
+// The two halves of the workgroup run half a tile apart (waves w and w + 4
+// share a SIMD): per 64-key tile u a wave runs an MFMA phase M(u) (the scores)
+// and a vector phase X(u) (the exponentials and this wave's column sums into
+// LDS); waves 0-3 run M(u) in slot 2u and X(u) in slot 2u+1, waves 4-7 one
+// slot later, so each SIMD has one wave on the matrix cores while the other
+// is on the vector ALU. Wave 0 adds the eight waves' column sums of tile u in
+// slot 2u+3, in wave order, and writes the mass. K tiles stream into a ring of
+// four LDS slots through direct-to-LDS DMA, three tiles ahead, issued by waves
+// 6 and 7 (half of each tile each) right after the barrier that opens an even
+// slot; each waits for its half of tile u before the barrier that opens slot
+// 2u, the first phase that reads it.
 template <int D, int RBW>
 __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassParams p) {
   constexpr int NW = kMassWaves, TK = kMassTile;
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
-  constexpr int KBYTES = TK * ROWB;
-  constexpr int CHUNKS = KBYTES / 16;           // 16-byte chunks per tile
-  constexpr int CPT = CHUNKS / (64 * NW);       // chunks per thread
+  constexpr int RPI = 1024 / ROWB;  // K rows per DMA instruction
+  constexpr int TB = TK * ROWB;     // bytes of a K tile
   constexpr int NSB = TK / 32;
   constexpr int KPB = D / 16;
-  static_assert(CHUNKS % (64 * NW) == 0, "whole chunks per thread");
-  __shared__ __attribute__((aligned(16))) char kbuf[2][KBYTES];
-  __shared__ float red[NW][TK];
+  constexpr int NS = 4;             // K ring slots
+  constexpr int KA = NS - 1;        // tiles issued ahead of the one being read
+  constexpr int NI = 2;             // issuing waves
+  constexpr int IPW = TB / 1024 / NI;
+  static_assert(IPW * NI * 1024 == TB && KA * IPW < 64, "DMA split");
+  __shared__ __attribute__((aligned(1024))) char kring[NS * TB];
+  __shared__ float red[2][NW][TK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int n = lane & 31;
   const int split = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / p.kv_heads;
   const int hkv = bh - b * p.kv_heads;
-  const int R = p.group * p.block_len;
   const int t0 = (int)((int64_t)split * p.tiles / p.splits);
   const int t1 = (int)((int64_t)(split + 1) * p.tiles / p.splits);
+  const int T = t1 - t0;
   const float c2 = p.scale_log2;
 
   // A-operand query fragments (row n of each block) and, for the 16 rows the
   // accumulator registers hold (row 8 (r / 4) + 4 h + r % 4 of the block),
-  // -LSE in base 2; rows past R get -inf, so their weights are exactly 0
+  // -LSE in base 2; rows past the pass get -inf, so their weights are exactly 0
   bf16x8_t qf[RBW][KPB];
   float nl2[RBW][16];
   bool has[RBW];
@@ -119,50 +135,47 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
       nl2[j][r] = v;
     }
   }
-  (void)R;
 
-  // K tile t: thread tid stages chunks tid + 512 * i; rows past the prefix read
-  // row 0 (their mass is never written)
+  // K tile u (keys (t0 + u) * TK ..) into ring slot u % NS: issuing wave i
+  // fills instructions i*IPW .. i*IPW + IPW - 1, RPI rows each, lane l the
+  // LDS chunk l % CPR of its row with logical chunk (l % CPR) ^ swizzle(row).
+  // Rows past the prefix read its last row (their mass is never written).
   const char* kbase = (const char*)p.k + 2 * ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh);
   const int64_t kst = 2 * p.k_st;
-  u32x4_t stage[CPT];
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
+  const bool issuer = wave >= NW - NI;  // wave-uniform
+  const int k0 = (wave - (NW - NI)) * IPW;
+  const uint32_t kring_lds = lds_addr(kring);
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    if (u >= T) return;
+    const uint32_t dst = kring_lds + (u % NS) * TB;
+    const int64_t key0 = (int64_t)(t0 + u) * TK;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 64 * NW * i;
-      const int row = c / CPR, ch = c - (c / CPR) * CPR;
-      int64_t key = (int64_t)t * TK + row;
-      key = key < p.n_keys ? key : 0;
-      stage[i] = *(const u32x4_t*)(kbase + key * kst + 16 * ch);
+    for (int j = 0; j < IPW; ++j) {
+      const int k = k0 + j;
+      const int r = k * RPI + lane / CPR;
+      int64_t key = key0 + r;
+      key = key < p.n_keys ? key : p.n_keys - 1;
+      const int lc = (lane % CPR) ^ mswz<CPR>(r);
+      dma_1k(kbase + key * kst + 16 * lc, dst + k * 1024);
     }
   };
-  auto store_tile = [&](int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 64 * NW * i;
-      const int row = c / CPR, ch = c - (c / CPR) * CPR;
-      *(u32x4_t*)(kbuf[slot] + row * ROWB + 16 * (ch ^ mswz<CPR>(row))) = stage[i];
-    }
+  // DMA instructions of this issuer for the tiles of [a, b] that exist
+  auto insts = [&](int a, int bb) __attribute__((always_inline)) {
+    const int lo = a > 0 ? a : 0;
+    const int hi = bb < T - 1 ? bb : T - 1;
+    return hi >= lo ? (hi - lo + 1) * IPW : 0;
   };
 
-  float* mrow = p.mass + ((int64_t)b * p.kv_heads + hkv) * p.n_keys;
-
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int t = t0; t < t1; ++t) {
-    const int cur = (t - t0) & 1;
-    if (t + 1 < t1) load_tile(t + 1);  // in flight while this tile is computed
-    const char* kb = kbuf[cur];
-    f32x16_t sacc[RBW][NSB];
+  f32x16_t sacc[RBW][NSB];
+  auto m_phase = [&](int u) __attribute__((always_inline)) {
+    const char* kb = kring + (u % NS) * TB;
 #pragma unroll
     for (int j = 0; j < RBW; ++j)
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[j][sb][r] = 0.0f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KPB; ++kk)
 #pragma unroll
@@ -175,7 +188,10 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
             sacc[j][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j][kk], __builtin_bit_cast(bf16x8_t, a),
                                                                   sacc[j][sb], 0, 0, 0);
       }
-    // column sums: key 32 sb + n over this wave's rows, fixed order (j, r)
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // column sums: key 32 sb + n over this wave's rows, fixed order (j, r)
+  auto x_phase = [&](int u) __attribute__((always_inline)) {
     float cs[NSB];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
@@ -190,18 +206,46 @@ __global__ __launch_bounds__(64 * kMassWaves) void mass_bf16_kernel(const MassPa
     }
     if (h == 0) {
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) red[wave][32 * sb + n] = cs[sb];
+      for (int sb = 0; sb < NSB; ++sb) red[u & 1][wave][32 * sb + n] = cs[sb];
     }
-    __syncthreads();  // red complete; every wave is done with kbuf[cur]
-    if (wave == 0) {
-      float s = 0.0f;
+  };
+  float* mrow = p.mass + ((int64_t)b * p.kv_heads + hkv) * p.n_keys;
+  auto reduce = [&](int u) __attribute__((always_inline)) {
+    float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += red[w][lane];
-      const int64_t key = (int64_t)t * TK + lane;
-      if (key < p.n_keys) mrow[key] = p.accumulate ? mrow[key] + s : s;
+    for (int w = 0; w < NW; ++w) sum += red[u & 1][w][lane];
+    const int64_t key = (int64_t)(t0 + u) * TK + lane;
+    if (key < p.n_keys) mrow[key] = p.accumulate ? mrow[key] + sum : sum;
+  };
+
+  wait_vm<0>();  // the query fragments have landed before any DMA is counted
+  if (issuer)
+    for (int u = 0; u < KA; ++u) issue(u);
+  // slot 2u: the issuers wait for their halves of tile u, barrier, issue
+  // tile u + KA; slot 2u + 1: barrier
+  auto even_slot = [&](int u) __attribute__((always_inline)) {
+    if (issuer) wait_at_most<(KA - 1) * IPW, IPW, 0>(insts(u + 1, u + KA - 1));
+    tile_barrier();
+    if (issuer) issue(u + KA);
+  };
+  if (wave < NW / 2) {
+    // leading half: M(u) in slot 2u, X(u) in slot 2u + 1; wave 0 reduces
+    // tile u - 1 in slot 2u + 1
+    for (int u = 0; u <= T; ++u) {
+      even_slot(u);
+      if (u < T) m_phase(u);
+      tile_barrier();
+      if (u < T) x_phase(u);
+      if (wave == 0 && u >= 1) reduce(u - 1);
     }
-    if (t + 1 < t1) store_tile(cur ^ 1);
-    __syncthreads();  // next tile staged; red read
+  } else {
+    // lagging half: X(u - 1) in slot 2u, M(u) in slot 2u + 1
+    for (int u = 0; u <= T; ++u) {
+      even_slot(u);
+      if (u >= 1) x_phase(u - 1);
+      tile_barrier();
+      if (u < T) m_phase(u);
+    }
   }
 }
 

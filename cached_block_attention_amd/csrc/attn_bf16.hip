@@ -20,8 +20,9 @@
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no
 //    register staging) into rings of LDS tiles, several tiles in flight. Rows
 //    are stored with an XOR swizzle of their 16-byte chunks, chosen on the
-//    global side of the DMA. Inside a dense prefix the source is a scalar tile
-//    base plus a per-lane 32-bit offset fixed for the whole loop.
+//    global side of the DMA. Where the workgroup has a wave that owns no rows,
+//    that wave (and, in the ping-pong kernel, one more) issues the DMAs, so
+//    the waves that compute never stall behind the memory pipeline.
 //  * Each wave owns 32 packed rows. Scores are computed transposed,
 //    S^T = K Q^T (v_mfma_f32_32x32x16_bf16; keys on the M side read from LDS,
 //    queries on the N side held in registers for the whole loop), so a lane
@@ -39,7 +40,7 @@
 //    sum of those rounded weights (v_dot2_f32_bf16 against (1, 1)), so o is an
 //    exact convex combination of V rows with the weights actually used; l and
 //    the log-sum-exp use the sum of the unrounded weights.
-//  * Eight-wave workgroups (more than 128 packed rows) run the two halves of
+//  * Eight-wave workgroups of 129 to 224 packed rows run the two halves of
 //    the workgroup half a tile apart ("ping-pong"): waves 0-3 and 4-7 share
 //    the four SIMDs pairwise, and while one wave of a pair issues the MFMAs of
 //    a tile (PV of the previous tile, then the scores of this one) the other

@@ -31,6 +31,10 @@ constexpr int64_t kComputeUnits = 256;
 // split-partial traffic (d+2 fp32 per row per split) relative to the K/V
 // stream.
 constexpr int64_t kMinTilesPerSplit = 4;
+// Finest packed-row chunk a small launch is cut into, and the longest key
+// range for which that is done (each chunk reads the range again).
+constexpr int64_t kMinChunkRows = 32;
+constexpr int64_t kFineChunkKeys = 8192;
 constexpr size_t kWsAlign = 256;
 
 int fail(int status, const char* fmt, ...) {
@@ -99,25 +103,9 @@ struct Plan {
   int splits = 1;
 };
 
-Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
-  Plan pl;
-  const int64_t G = d->q_heads / d->kv_heads;
-  const int64_t R = G * d->block_len;
-  int64_t base, per_cu = 1;
-  if (d->dtype == BLKATTN_F32) {
-    pl.tile_keys = 32;
-    base = (int64_t)d->batch * d->q_heads;
-    per_cu = 8;
-  } else {
-    pl.row_chunks = R > 256 ? (int)((R + 255) / 256) : 1;
-    const int64_t rows = (R + pl.row_chunks - 1) / pl.row_chunks;
-    pl.waves = bf16_waves_for_rows(rows);
-    pl.rows_per_wg = (int)(32 * ((rows + 31) / 32));  // whole 32-row waves per chunk
-    pl.tile_keys = bf16_tile_keys(pl.waves);
-    base = (int64_t)d->batch * d->kv_heads * pl.row_chunks;
-    per_cu = bf16_workgroups_per_cu(pl.waves);
-  }
-  pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
+// Key splits for a chunking of the packed rows (bf16) or for the fp32 kernel.
+int64_t plan_splits(const blkattn_dims* d, const Plan& pl, int64_t base, int64_t per_cu, int64_t n_keys,
+                    bool indexed) {
   const int64_t tiles64 = (n_keys + 63) / 64;
   int64_t s;
   if (d->splits > 0) {
@@ -137,7 +125,37 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
     const int64_t need = (pl.tiles + per - 1) / per;
     if (s < need) s = need;
   }
-  pl.splits = (int)s;
+  return s;
+}
+
+Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
+  Plan pl;
+  const int64_t G = d->q_heads / d->kv_heads;
+  const int64_t R = G * d->block_len;
+  if (d->dtype == BLKATTN_F32) {
+    pl.tile_keys = 32;
+    pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
+    pl.splits = (int)plan_splits(d, pl, (int64_t)d->batch * d->q_heads, 8, n_keys, indexed);
+    return pl;
+  }
+  // Packed-row chunks of at most `cap` rows, one workgroup each per key split.
+  // The cap starts at 256 (eight waves); when the launch would still hold
+  // fewer workgroups than the GPU has compute units (a short key range that
+  // cannot be split further, as in a large block's own keys), it is halved,
+  // down to one wave: every chunk then reads the key range again, which costs
+  // little when the range is this short.
+  for (int64_t cap = 256;; cap /= 2) {
+    pl.row_chunks = R > cap ? (int)((R + cap - 1) / cap) : 1;
+    const int64_t rows = (R + pl.row_chunks - 1) / pl.row_chunks;
+    pl.waves = bf16_waves_for_rows(rows);
+    pl.rows_per_wg = (int)(32 * ((rows + 31) / 32));  // whole 32-row waves per chunk
+    pl.tile_keys = bf16_tile_keys(pl.waves);
+    pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
+    const int64_t base = (int64_t)d->batch * d->kv_heads * pl.row_chunks;
+    const int64_t s = plan_splits(d, pl, base, bf16_workgroups_per_cu(pl.waves), n_keys, indexed);
+    pl.splits = (int)s;
+    if (base * s >= kComputeUnits || cap <= kMinChunkRows || R <= 32 || n_keys > kFineChunkKeys) break;
+  }
   return pl;
 }
 

@@ -229,7 +229,9 @@ def test_block_step_continues_the_cached_state(ba, name, kw):
     eo, el = max_err(down(o), o_ref), max_err(down(lse), lse_ref)
     say(f"  block step err O {eo:.3e} LSE {el:.3e}")
     assert eo <= tol["o"] and el <= tol["lse"], (eo, el)
-    assert max_err(down(o), down(o2)) <= tol["o"] and max_err(down(lse), down(lse2)) <= tol["lse"]
+    # two results each within tol of the oracle are within 2 tol of each other;
+    # their bf16 roundings need not coincide (one ulp is 0.0156 for |O| in [2, 4))
+    assert max_err(down(o), down(o2)) <= 2 * tol["o"] and max_err(down(lse), down(lse2)) <= 2 * tol["lse"]
 
 
 def test_block_step_from_empty_and_from_other_queries(ba):

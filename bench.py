@@ -369,6 +369,57 @@ def extra_lines(reps: int, paths=EXTRA_PATHS):
         torch.cuda.empty_cache()
 
 
+def power_line(step, seconds: float, sh: datagen.Shape):
+    """Run `step` back to back for `seconds` while another thread samples the
+    board (amd-smi metric -p -c) every 0.2 s; print the step time and the
+    median socket power and graphics clock of the samples."""
+    import subprocess
+    import threading
+    import torch
+
+    samples, stop = [], [False]
+
+    def sample():
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True)
+        try:
+            d = json.loads(r.stdout)
+            g = d[0] if isinstance(d, list) else d
+            g = g["gpu_data"][0] if "gpu_data" in g else g
+            clocks = [v["clk"]["value"] for k, v in g["clock"].items()
+                      if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                      and isinstance(v["clk"].get("value"), (int, float))]
+            return float(g["power"]["socket_power"]["value"]), float(np.mean(clocks))
+        except (ValueError, KeyError, TypeError, IndexError):
+            return None
+
+    def sampler():
+        while not stop[0]:
+            x = sample()
+            if x is not None:
+                samples.append(x)
+            time.sleep(0.2)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(100):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stop[0] = True
+    th.join()
+    tail = samples[len(samples) // 3:]  # after the first third, once power has settled
+    print(json.dumps({
+        "power_run": sh.name, "seconds": round(dt, 2), "steps": n, "ms_per_step": round(dt / n * 1e3, 5),
+        "samples": len(tail),
+        "socket_power_w_median": float(np.median([x[0] for x in tail])) if tail else None,
+        "gfx_clock_mhz_median": float(np.median([x[1] for x in tail])) if tail else None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +432,9 @@ def main():
     ap.add_argument("--path", default="full", choices=["full", "cached"],
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power", type=float, metavar="SECONDS",
+                    help="after the warmup, run the step back to back for SECONDS while sampling board power "
+                         "and clocks with amd-smi; print one JSON line and exit")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write the --traffic record from the four rocprofv3 counter runs under DIR")
@@ -450,6 +504,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.power:
+        power_line(step, args.power, sh)
+        return
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]

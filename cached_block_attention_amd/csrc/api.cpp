@@ -34,6 +34,8 @@ constexpr int64_t kMinTilesPerSplit = 4;
 // Finest packed-row chunk a small launch is cut into, and the longest key
 // range for which that is done (each chunk reads the range again).
 constexpr int64_t kMinChunkRows = 32;
+// The MI355X last-level (Infinity) cache.
+constexpr int64_t kLastLevelCacheBytes = (int64_t)256 << 20;
 constexpr int64_t kFineChunkKeys = 8192;
 constexpr size_t kWsAlign = 256;
 
@@ -231,7 +233,14 @@ AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Pla
   return p;
 }
 
-int launch_attn(const blkattn_dims* d, const AttnParams& p, const Plan& pl, hipStream_t stream) {
+int launch_attn(const blkattn_dims* d, const AttnParams& p0, const Plan& pl, hipStream_t stream) {
+  // A dense prefix whose K/V (as read by this launch: once per row chunk)
+  // exceeds the last-level cache is streamed with non-temporal loads; shorter
+  // ones keep the normal policy, so that repeated calls can hit the cache.
+  AttnParams p = p0;
+  const int64_t kv_bytes = 2 * (int64_t)d->batch * d->kv_heads * pl.row_chunks * p.keys.n_pre * d->head_dim *
+                           elt_bytes(d->dtype);
+  p.keys.stream_nt = p.keys.idx == nullptr && pl.row_chunks == 1 && kv_bytes > kLastLevelCacheBytes;
   KernelEvents ev;
   ev.start = (hipEvent_t)g_ev_start;
   ev.stop = (hipEvent_t)g_ev_stop;

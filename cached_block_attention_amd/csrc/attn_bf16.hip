@@ -108,7 +108,7 @@ struct KeyRows {
   const char* vblk;
   int64_t kp_st, vp_st, kb_st, vb_st;  // row strides in bytes
   int64_t n_pre, n_all, hole, hole_len;
-  bool indexed, off32, gather32;
+  bool indexed, off32, gather32, nt;
 };
 
 // A tile whose rows all come from one strided segment: the dense prefix on
@@ -118,6 +118,7 @@ struct SegTile {
   const char* base;  // row 0 of the tile
   int64_t st;        // row stride in bytes
   int valid;         // rows inside the segment
+  bool nt;           // dense prefix rows of a long single-pass stream: non-temporal loads
 };
 
 template <int TK>
@@ -135,16 +136,18 @@ __device__ __forceinline__ SegTile seg_tile(const KeyRows& kr, bool isv, int64_t
     f.base = (isv ? kr.vblk : kr.kblk) + (key0 - kr.n_pre) * f.st;
     const int64_t left = kr.n_all - key0;
     f.valid = left < TK ? (int)left : TK;
+    f.nt = false;
   } else {
     f.st = isv ? kr.vp_st : kr.kp_st;
     f.base = (isv ? kr.vpre : kr.kpre) + (key0 + (key0 >= kr.hole ? kr.hole_len : 0)) * f.st;
     f.valid = TK;
+    f.nt = kr.nt;
   }
   f.base = uniform_ptr(f.base);
   return f;
 }
 
-template <int D, int TK>
+template <int D, int TK, bool NT = false>
 __device__ __forceinline__ void dma_one_fast(const SegTile& f, bool isv, uint32_t dst, int k, int lane) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
@@ -153,7 +156,7 @@ __device__ __forceinline__ void dma_one_fast(const SegTile& f, bool isv, uint32_
   const int r = k * RPI + ln / CPR;
   const int rs = r < f.valid ? r : f.valid - 1;
   const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
-  dma_1k_s(f.base, (uint32_t)rs * (uint32_t)f.st + 16 * lc, dst + k * 1024);
+  dma_1k_s<NT>(f.base, (uint32_t)rs * (uint32_t)f.st + 16 * lc, dst + k * 1024);
 }
 
 // A tile of retained (gathered) prefix rows whose byte offsets from the head's
@@ -228,8 +231,13 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
   constexpr int INT = TK * D * 2 / 1024;
   if (tile_is_fast<TK>(kr, key0)) {
     const SegTile f = seg_tile<TK>(kr, isv, key0);
+    if (f.nt) {
 #pragma unroll
-    for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(f, isv, dst, k, lane);
+      for (int k = 0; k < INT; ++k) dma_one_fast<D, TK, true>(f, isv, dst, k, lane);
+    } else {
+#pragma unroll
+      for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(f, isv, dst, k, lane);
+    }
     return;
   }
   if (tile_is_gather<TK>(kr, key0)) {
@@ -514,6 +522,7 @@ __device__ __forceinline__ Setup<D> setup(const AttnParams& p, int32_t* sidx, in
   kr.indexed = p.keys.idx != nullptr;
   kr.off32 = p.keys.off32 != 0;
   kr.gather32 = p.keys.gather32 != 0;
+  kr.nt = p.keys.stream_nt != 0 && !kr.indexed;
 
   // retained-row indices of this split's prefix keys, staged in LDS
   if (kr.indexed) {

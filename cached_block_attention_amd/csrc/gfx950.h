@@ -35,25 +35,46 @@ __device__ __forceinline__ void tile_barrier() {
 // asm so that the compiler does not see an LDS write in flight and drain the
 // whole DMA ring (vmcnt(0)) before every LDS read; completion is ordered
 // explicitly by vmcnt waits before the tile barriers. The instruction has no
-// register results.
+// register results. NT marks the load non-temporal (streamed once: the caches
+// need not keep it), which lets a long single-pass stream run faster.
+template <bool NT = false>
 __device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
-  __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
-      : "memory", "m0");
+  if constexpr (NT) {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off nt"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+        : "memory", "m0");
+  } else {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+        : "memory", "m0");
+  }
 }
 
 // The same DMA from a wave-uniform base in scalar registers plus a per-lane
 // unsigned 32-bit byte offset.
+template <bool NT = false>
 __device__ __forceinline__ void dma_1k_s(const char* sbase, uint32_t voff, uint32_t lds_addr) {
-  __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
-      : "memory", "m0");
+  if constexpr (NT) {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+        : "memory", "m0");
+  } else {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+        : "memory", "m0");
+  }
 }
 
 // A wave-uniform pointer moved to scalar registers.

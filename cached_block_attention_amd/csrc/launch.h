@@ -26,6 +26,7 @@ struct KeySeq {
   int64_t k_hole, k_hole_len;
   int32_t off32;                // byte offsets within any 64-row tile (prefix or block) fit 31 bits
   int32_t gather32;             // with idx: byte offsets of every prefix row (p_rows of them) fit 31 bits
+  int32_t stream_nt;            // dense prefix tiles are loaded non-temporal (a long single-pass stream)
   const void* k_blk;
   const void* v_blk;
   int64_t kb_sb, kb_sh, kb_st;

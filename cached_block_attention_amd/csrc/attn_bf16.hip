@@ -108,7 +108,7 @@ struct KeyRows {
   const char* vblk;
   int64_t kp_st, vp_st, kb_st, vb_st;  // row strides in bytes
   int64_t n_pre, n_all, hole, hole_len;
-  bool indexed, off32, gather32, nt;
+  bool indexed, off32, gather32;
 };
 
 // A tile whose rows all come from one strided segment: the dense prefix on
@@ -118,7 +118,6 @@ struct SegTile {
   const char* base;  // row 0 of the tile
   int64_t st;        // row stride in bytes
   int valid;         // rows inside the segment
-  bool nt;           // dense prefix rows of a long single-pass stream: non-temporal loads
 };
 
 template <int TK>
@@ -136,12 +135,10 @@ __device__ __forceinline__ SegTile seg_tile(const KeyRows& kr, bool isv, int64_t
     f.base = (isv ? kr.vblk : kr.kblk) + (key0 - kr.n_pre) * f.st;
     const int64_t left = kr.n_all - key0;
     f.valid = left < TK ? (int)left : TK;
-    f.nt = false;
   } else {
     f.st = isv ? kr.vp_st : kr.kp_st;
     f.base = (isv ? kr.vpre : kr.kpre) + (key0 + (key0 >= kr.hole ? kr.hole_len : 0)) * f.st;
     f.valid = TK;
-    f.nt = kr.nt;
   }
   f.base = uniform_ptr(f.base);
   return f;
@@ -224,20 +221,16 @@ __device__ __forceinline__ void dma_one(const KeyRows& kr, bool isv, int64_t key
 // The whole DMA of one K (or V) tile, issued by one wave. On the fast path
 // each instruction is a scalar base plus a per-lane offset recomputed from the
 // lane index (a few VALU operations, no registers held across the loop); the
-// other tiles loop over the general form without unrolling it.
-template <int D, int TK>
+// other tiles loop over the general form without unrolling it. With NT the
+// strided tiles (dense prefix and block) are loaded non-temporal.
+template <int D, int TK, bool NT = false>
 __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int lane,
                                              const int32_t* sidx, int64_t kbeg) {
   constexpr int INT = TK * D * 2 / 1024;
   if (tile_is_fast<TK>(kr, key0)) {
     const SegTile f = seg_tile<TK>(kr, isv, key0);
-    if (f.nt) {
 #pragma unroll
-      for (int k = 0; k < INT; ++k) dma_one_fast<D, TK, true>(f, isv, dst, k, lane);
-    } else {
-#pragma unroll
-      for (int k = 0; k < INT; ++k) dma_one_fast<D, TK>(f, isv, dst, k, lane);
-    }
+    for (int k = 0; k < INT; ++k) dma_one_fast<D, TK, NT>(f, isv, dst, k, lane);
     return;
   }
   if (tile_is_gather<TK>(kr, key0)) {
@@ -522,7 +515,6 @@ __device__ __forceinline__ Setup<D> setup(const AttnParams& p, int32_t* sidx, in
   kr.indexed = p.keys.idx != nullptr;
   kr.off32 = p.keys.off32 != 0;
   kr.gather32 = p.keys.gather32 != 0;
-  kr.nt = p.keys.stream_nt != 0 && !kr.indexed;
 
   // retained-row indices of this split's prefix keys, staged in LDS
   if (kr.indexed) {
@@ -684,7 +676,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 // tile; with DMAW one more wave (wave NW, no rows) issues them all instead, so
 // that a row wave never stalls behind the memory pipeline between its
 // products.
-template <int D, int NW, int TK, int NS, bool DMAW = false>
+template <int D, int NW, int TK, int NS, bool DMAW = false, bool NT = false>
 __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnParams p) {
   constexpr int TB = TK * D * 2;                       // bytes of a K (or V) tile
   constexpr int IPW = DMAW ? TB / 1024 : TB / 1024 / NW;  // DMA instructions per issuing wave per K (or V) tile
@@ -711,8 +703,8 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
     const uint32_t slot = ring_lds + (t % NS) * 2 * TB;
     const int64_t key0 = s.kbeg + (int64_t)t * TK;
     if (DMAW) {
-      dma_tile_all<D, TK>(s.kr, false, key0, slot, lane, sidx, s.kbeg);
-      dma_tile_all<D, TK>(s.kr, true, key0, slot + TB, lane, sidx, s.kbeg);
+      dma_tile_all<D, TK, NT>(s.kr, false, key0, slot, lane, sidx, s.kbeg);
+      dma_tile_all<D, TK, NT>(s.kr, true, key0, slot + TB, lane, sidx, s.kbeg);
     } else {
       dma_tile<D, TK, NW>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
       dma_tile<D, TK, NW>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
@@ -762,7 +754,7 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
 // tile t-1 is still being read). Both issue right after a barrier and wait
 // for their tiles to land just before one, so that no computing wave waits
 // behind the memory pipeline in the middle of a phase.
-template <int D>
+template <int D, bool NT = false>
 __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   constexpr int NW = 8;
   constexpr int TK = 64;
@@ -800,7 +792,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
     if (!in_range(tt)) return;
     const int64_t key0 = s.kbeg + (int64_t)tt * TK;
     const uint32_t dst = isv ? vring_lds + (tt % NSV) * TB : kring_lds + (tt % NSK) * TB;
-    dma_tile_all<D, TK>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
+    dma_tile_all<D, TK, NT>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
   };
   // Tiles of [a, b] that exist, times the DMAs per tile.
   auto insts = [&](int a, int b) __attribute__((always_inline)) {
@@ -901,12 +893,20 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
 template <int D, int NW>
 hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev) {
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
+  const bool nt = p.keys.stream_nt != 0;  // a dense prefix longer than the last-level cache
   if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
-    hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+    if (nt)
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else if (NW == 1 && p.tiles >= 4 * p.splits) {
     // one row wave over a long key range: a second wave issues the DMAs
-    hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
-                          p);
+    if (nt)
+      hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true, true>), grid, dim3(128), 0, stream, ev.start,
+                            ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
+                            p);
   } else {
     constexpr int TK = NW == 1 ? 32 : 64;
     constexpr int NS = 4;

@@ -453,8 +453,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the path shards "
-              "over (batch, kv-head) groups with no communication, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the path would shard "
+              "over (batch, kv-head) groups with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -19,7 +19,7 @@ Sources (the pages this follows):
   [kv state]   aitopics tag page "kv state", Sparse-dLLM abstract: retained
                critical tokens, evicted others (attention over a kept subset).
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   * scores carry an explicit scale: s = scale * <q, k> (the pages print QK^T;
     the scale is a float argument, 1/sqrt(d) in every workload), and the oracle
     uses that float32 value exactly;

@@ -140,9 +140,71 @@ def _dtype_code(t) -> int:
 
 
 def _check_gpu(*ts):
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("blkattn runs on the GPU only: every tensor must be a CUDA/HIP tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _expect(t, name: str, shape, dtype=None, contiguous: bool = False, optional: bool = False):
+    """Raise ValueError unless `t` has exactly `shape` (and `dtype`, and is
+    contiguous when asked). The C ABI takes pointers and one set of sizes, so a
+    tensor that disagrees with those sizes would be read or written out of
+    bounds by the kernels: every argument is checked here first."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dim() != len(shape) or tuple(int(x) for x in t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_partial_shape(p, name: str, B: int, Hq: int, rows: int, d: int, optional: bool = False):
+    torch = _torch()
+    if p is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    _expect(p.o, f"{name}.o", (B, Hq, rows, d), torch.float32, contiguous=True)
+    _expect(p.m, f"{name}.m", (B, Hq, rows), torch.float32, contiguous=True)
+    _expect(p.l, f"{name}.l", (B, Hq, rows), torch.float32, contiguous=True)
+
+
+def _check_qkv(q, k, v, k_name: str, v_name: str, rows=None):
+    """q [B, Hq, T, d]; k, v [B, Hkv, rows, d] of q's dtype with Hq % Hkv == 0."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, T, d], got shape {tuple(q.shape)}")
+    _dtype_code(q)
+    B, Hq, _, d = q.shape
+    if k.dim() != 4:
+        raise ValueError(f"{k_name} must be [B, H, T, d], got shape {tuple(k.shape)}")
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the {Hkv} heads of {k_name}")
+    n = k.shape[2] if rows is None else rows
+    _expect(k, k_name, (B, Hkv, n, d), q.dtype)
+    _expect(v, v_name, (B, Hkv, n, d), q.dtype)
+    return B, Hq, Hkv, d
+
+
+def _check_idx(idx, B: int, Hkv: int):
+    torch = _torch()
+    if idx is None:
+        return 0
+    if idx.dim() != 3:
+        raise ValueError(f"idx must be [B, Hkv, n_keep], got shape {tuple(idx.shape)}")
+    _expect(idx, "idx", (B, Hkv, idx.shape[2]), torch.int32, contiguous=True)
+    return int(idx.shape[2])
 
 
 def _tensor(t) -> Optional[Tensor]:
@@ -241,8 +303,15 @@ def set_kernel_events(start, stop):
 def blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=None, splits=0,
                  workspace=None, stream=None):
     """O (and LSE) of the block queries over [prefix (or its idx rows); block]."""
+    torch = _torch()
+    B, Hq, Hkv, d = _check_qkv(q, k_pre, v_pre, "k_pre", "v_pre")
+    Bq = q.shape[2]
+    _expect(k_blk, "k_blk", (B, Hkv, Bq, d), q.dtype)
+    _expect(v_blk, "v_blk", (B, Hkv, Bq, d), q.dtype)
+    _expect(o, "o", (B, Hq, Bq, d), q.dtype)
+    _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
+    n_keep = _check_idx(idx, B, Hkv)
     _check_gpu(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx)
-    n_keep = int(idx.shape[-1]) if idx is not None else 0
     dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
     ws, nbytes = _workspace(dims, OP_FULL, q.device, workspace)
     st = library().blkattn_full(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
@@ -256,8 +325,10 @@ def blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=Non
 def blkattn_prefix_partial(q, k_pre, v_pre, out: Partial, idx=None, scale=None, splits=0,
                            workspace=None, stream=None):
     """Partial state of the block queries over the prefix (the FACache state)."""
+    B, Hq, Hkv, d = _check_qkv(q, k_pre, v_pre, "k_pre", "v_pre")
+    _check_partial_shape(out, "out", B, Hq, q.shape[2], d)
+    n_keep = _check_idx(idx, B, Hkv)
     _check_gpu(q, k_pre, v_pre, idx, *out)
-    n_keep = int(idx.shape[-1]) if idx is not None else 0
     dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
     ws, nbytes = _workspace(dims, OP_PREFIX_PARTIAL, q.device, workspace)
     st = library().blkattn_prefix_partial(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
@@ -269,6 +340,8 @@ def blkattn_prefix_partial(q, k_pre, v_pre, out: Partial, idx=None, scale=None, 
 
 def blkattn_block_partial(q, k_blk, v_blk, out: Partial, scale=None, stream=None):
     """Partial state of the block queries over the block's own keys (no mask)."""
+    B, Hq, _, d = _check_qkv(q, k_blk, v_blk, "k_blk", "v_blk", rows=q.shape[2] if q.dim() == 4 else None)
+    _check_partial_shape(out, "out", B, Hq, q.shape[2], d)
     _check_gpu(q, k_blk, v_blk, *out)
     dims = make_dims(q, k_blk.shape[1], 0, 0, scale, 0)
     st = library().blkattn_block_partial(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_blk)),
@@ -280,6 +353,12 @@ def blkattn_block_partial(q, k_blk, v_blk, out: Partial, scale=None, stream=None
 def blkattn_block_step(q, k_blk, v_blk, cached: Partial, o, lse=None, scale=None, stream=None):
     """One reuse step in one launch: the block queries' state starts from the cached
     prefix partial and continues over the block's own keys; writes O and LSE."""
+    torch = _torch()
+    B, Hq, _, d = _check_qkv(q, k_blk, v_blk, "k_blk", "v_blk", rows=q.shape[2] if q.dim() == 4 else None)
+    Bq = q.shape[2]
+    _check_partial_shape(cached, "cached", B, Hq, Bq, d)
+    _expect(o, "o", (B, Hq, Bq, d), q.dtype)
+    _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
     _check_gpu(q, k_blk, v_blk, *cached, o, lse)
     dims = make_dims(q, k_blk.shape[1], 0, 0, scale, 0)
     st = library().blkattn_block_step(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_blk)),
@@ -295,8 +374,13 @@ def blkattn_sequence_step(q, k, v, block_start: int, block_len: int, cache: Part
     [B, Hkv, N, d]) at one step of the block at rows [block_start, +block_len),
     with the FACache of the other rows' queries over the other rows' keys:
     built when gen_step is true, reused otherwise. Writes o and lse [B, Hq, N]."""
+    torch = _torch()
+    B, Hq, _, d = _check_qkv(q, k, v, "k", "v", rows=q.shape[2] if q.dim() == 4 else None)
+    N = q.shape[2]
+    _check_partial_shape(cache, "cache", B, Hq, N, d)
+    _expect(o, "o", (B, Hq, N, d), q.dtype)
+    _expect(lse, "lse", (B, Hq, N), torch.float32, contiguous=True, optional=True)
     _check_gpu(q, k, v, *cache, o, lse)
-    B, Hq, N, d = q.shape
     dims = Dims(B, Hq, k.shape[1], d, int(block_len), 0, N, _dtype_code(q),
                 float(1.0 / math.sqrt(d) if scale is None else scale), splits, 0)
     ws, nbytes = _workspace(dims, OP_SEQUENCE, q.device, workspace)
@@ -312,8 +396,17 @@ def blkattn_merge(a: Partial, b: Partial, o=None, lse=None, ab: Optional[Partial
                   dtype=None, stream=None):
     """Log-sum-exp merge of two partials; writes O (dtype of `o`), LSE and/or `ab`."""
     torch = _torch()
-    _check_gpu(*a, *b, o, lse, *(ab or ()))
+    if a.o.dim() != 4:
+        raise ValueError(f"a.o must be [B, Hq, Bq, d], got shape {tuple(a.o.shape)}")
     B, Hq, Bq, d = a.o.shape
+    _check_partial_shape(a, "a", B, Hq, Bq, d)
+    _check_partial_shape(b, "b", B, Hq, Bq, d)
+    _check_partial_shape(ab, "ab", B, Hq, Bq, d, optional=True)
+    if o is not None:
+        _dtype_code(o)
+        _expect(o, "o", (B, Hq, Bq, d))
+    _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
+    _check_gpu(*a, *b, o, lse, *(ab or ()))
     code = _dtype_code(o) if o is not None else (BF16 if dtype == torch.bfloat16 else F32)
     dims = Dims(B, Hq, 1, d, Bq, 0, 0, code, 1.0, 0, 0)
     st = library().blkattn_merge(ctypes.byref(dims), _ref(_partial(a)), _ref(_partial(b)),
@@ -324,8 +417,17 @@ def blkattn_merge(a: Partial, b: Partial, o=None, lse=None, ab: Optional[Partial
 
 def blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=None):
     """Bit copy of the retained prefix rows named by idx."""
-    _check_gpu(k_full, v_full, idx, k_out, v_out)
+    if k_full.dim() != 4:
+        raise ValueError(f"k_full must be [B, Hkv, P, d], got shape {tuple(k_full.shape)}")
+    _dtype_code(k_full)
     B, Hkv, P, d = k_full.shape
+    _expect(v_full, "v_full", (B, Hkv, P, d), k_full.dtype)
+    n = _check_idx(idx, B, Hkv) if idx is not None else None
+    if n is None:
+        raise ValueError("idx is required")
+    _expect(k_out, "k_out", (B, Hkv, n, d), k_full.dtype)
+    _expect(v_out, "v_out", (B, Hkv, n, d), k_full.dtype)
+    _check_gpu(k_full, v_full, idx, k_out, v_out)
     dims = Dims(B, Hkv, Hkv, d, 1, int(idx.shape[-1]), P, _dtype_code(k_full), 1.0, 0, 0)
     st = library().blkattn_gather_prefix(ctypes.byref(dims), _ref(_tensor(k_full)), _ref(_tensor(v_full)),
                                          _ptr(idx), _ref(_tensor(k_out)), _ref(_tensor(v_out)),
@@ -337,6 +439,12 @@ def blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=None):
 def blkattn_prefix_mass(q, k_pre, lse, mass, scale=None, stream=None):
     """Attention mass of every prefix row (summed probabilities over the block
     queries of the kv group), given each row's LSE over all keys."""
+    torch = _torch()
+    if k_pre.dim() != 4:
+        raise ValueError(f"k_pre must be [B, Hkv, P, d], got shape {tuple(k_pre.shape)}")
+    B, Hq, Hkv, d = _check_qkv(q, k_pre, k_pre, "k_pre", "k_pre")
+    _expect(lse, "lse", (B, Hq, q.shape[2]), torch.float32, contiguous=True)
+    _expect(mass, "mass", (B, Hkv, k_pre.shape[2]), torch.float32, contiguous=True)
     _check_gpu(q, k_pre, lse, mass)
     dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], 0, scale, 0)
     st = library().blkattn_prefix_mass(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
@@ -347,8 +455,17 @@ def blkattn_prefix_mass(q, k_pre, lse, mass, scale=None, stream=None):
 
 def blkattn_select_retained(mass, idx, workspace=None, stream=None):
     """The idx.shape[-1] rows of largest mass per (batch, kv head), ascending."""
-    _check_gpu(mass, idx)
+    torch = _torch()
+    if mass.dim() != 3:
+        raise ValueError(f"mass must be [B, Hkv, P], got shape {tuple(mass.shape)}")
     B, Hkv, P = mass.shape
+    _expect(mass, "mass", (B, Hkv, P), torch.float32, contiguous=True)
+    n = _check_idx(idx, B, Hkv) if idx is not None else None
+    if n is None:
+        raise ValueError("idx is required")
+    if n > P:
+        raise ValueError(f"idx asks for {n} rows of {P}")
+    _check_gpu(mass, idx)
     dims = Dims(B, Hkv, Hkv, 64, 1, int(idx.shape[-1]), P, F32, 1.0, 0, 0)
     ws, nbytes = _workspace(dims, OP_SELECT, mass.device, workspace)
     st = library().blkattn_select_retained(ctypes.byref(dims), _ptr(mass), _ptr(idx), _ptr(ws), nbytes,

@@ -235,12 +235,13 @@ AttnParams attn_params(const blkattn_dims* d, const blkattn_tensor* q, const Pla
 
 int launch_attn(const blkattn_dims* d, const AttnParams& p0, const Plan& pl, hipStream_t stream) {
   // A dense prefix whose K/V (as read by this launch: once per row chunk)
-  // exceeds the last-level cache is streamed with non-temporal loads; shorter
-  // ones keep the normal policy, so that repeated calls can hit the cache.
+  // fills the last-level cache is streamed with non-temporal loads: no later
+  // call can find it cached. Shorter ones keep the normal policy, so that
+  // repeated calls can hit the cache.
   AttnParams p = p0;
   const int64_t kv_bytes = 2 * (int64_t)d->batch * d->kv_heads * pl.row_chunks * p.keys.n_pre * d->head_dim *
                            elt_bytes(d->dtype);
-  p.keys.stream_nt = p.keys.idx == nullptr && pl.row_chunks == 1 && kv_bytes > kLastLevelCacheBytes;
+  p.keys.stream_nt = p.keys.idx == nullptr && pl.row_chunks == 1 && kv_bytes >= kLastLevelCacheBytes;
   KernelEvents ev;
   ev.start = (hipEvent_t)g_ev_start;
   ev.stop = (hipEvent_t)g_ev_stop;

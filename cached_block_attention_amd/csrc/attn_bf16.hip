@@ -156,6 +156,35 @@ __device__ __forceinline__ void dma_one_fast(const SegTile& f, bool isv, uint32_
   dma_1k_s<NT>(f.base, (uint32_t)rs * (uint32_t)f.st + 16 * lc, dst + k * 1024);
 }
 
+// A whole tile of contiguous rows (row stride = row bytes): 16 KB of memory
+// onto 16 KB of LDS. Its DMAs go in groups of four that share the scalar base
+// and M0 (instruction offsets 0, 1 KB, 2 KB, 3 KB), and a lane's offset within
+// a group is a swizzle pattern that depends only on the DMA's place in the
+// group (and for D = 64 on the group's parity), so the whole issue costs a
+// few vector instructions instead of an address computation per DMA.
+template <int D, int TK, bool NT = false>
+__device__ __forceinline__ void dma_tile_contig(const char* sbase, bool isv, uint32_t dst, int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int INT = TK * ROWB / 1024;
+  static_assert(INT % 4 == 0, "whole groups of four DMAs");
+  const int ln = opaque(lane);
+  const int rl = ln / CPR;
+  const int cl = ln % CPR;
+#pragma unroll
+  for (int g = 0; g < INT / 4; ++g) {
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (4 * g + i) * RPI + rl;
+      const int lc = cl ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+      v[i] = (uint32_t)(rl * ROWB + 16 * lc);
+    }
+    dma_4k_s<NT>(sbase + 4096 * g, v[0], v[1], v[2], v[3], dst + 4096 * g);
+  }
+}
+
 // A tile of retained (gathered) prefix rows whose byte offsets from the head's
 // first row fit 31 bits: scalar head base plus per-lane offsets from the
 // staged indices.
@@ -229,6 +258,10 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
   constexpr int INT = TK * D * 2 / 1024;
   if (tile_is_fast<TK>(kr, key0)) {
     const SegTile f = seg_tile<TK>(kr, isv, key0);
+    if (f.valid == TK && f.st == 2 * D) {
+      dma_tile_contig<D, TK, NT>(f.base, isv, dst, lane);
+      return;
+    }
 #pragma unroll
     for (int k = 0; k < INT; ++k) dma_one_fast<D, TK, NT>(f, isv, dst, k, lane);
     return;

@@ -31,7 +31,9 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 // One direct-to-LDS DMA: 64 lanes x 16 bytes from per-lane global addresses
-// into 1 KB of LDS at lds_addr (wave-uniform, through M0). Written as inline
+// into 1 KB of LDS at lds_addr (wave-uniform, through M0). A scalar write of
+// M0 needs one wait state before an LDS-DMA load reads it (the s_nop 0, which
+// the compiler cannot insert inside one asm statement). Written as inline
 // asm so that the compiler does not see an LDS write in flight and drain the
 // whole DMA ring (vmcnt(0)) before every LDS read; completion is ordered
 // explicitly by vmcnt waits before the tile barriers. The instruction has no
@@ -42,6 +44,7 @@ __device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
   if constexpr (NT) {
     __asm__ __volatile__(
         "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off nt"
         :
         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
@@ -49,6 +52,7 @@ __device__ __forceinline__ void dma_1k(const void* gptr, uint32_t lds_addr) {
   } else {
     __asm__ __volatile__(
         "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off"
         :
         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
@@ -63,6 +67,7 @@ __device__ __forceinline__ void dma_1k_s(const char* sbase, uint32_t voff, uint3
   if constexpr (NT) {
     __asm__ __volatile__(
         "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2 nt"
         :
         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
@@ -70,9 +75,42 @@ __device__ __forceinline__ void dma_1k_s(const char* sbase, uint32_t voff, uint3
   } else {
     __asm__ __volatile__(
         "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2"
         :
         : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+        : "memory", "m0");
+  }
+}
+
+// Four DMAs of 1 KB from a wave-uniform base in scalar registers: DMA i reads
+// 16 bytes per lane at sbase + voff_i + 1024*i and writes them to LDS at
+// lds_addr + 1024*i + 16*lane. The instruction offset moves the global and
+// the LDS address alike, so the four share one M0 write and one base.
+template <bool NT = false>
+__device__ __forceinline__ void dma_4k_s(const char* sbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                         uint32_t lds_addr) {
+  if constexpr (NT) {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5 nt\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:2048 nt\n\t"
+        "global_load_lds_dwordx4 %4, %5 offset:3072 nt"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(sbase)
+        : "memory", "m0");
+  } else {
+    __asm__ __volatile__(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %5 offset:3072"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(sbase)
         : "memory", "m0");
   }
 }

@@ -169,3 +169,72 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 32, 64)
     with pytest.raises(ValueError):
         ba.attention(q, q, q, q, q)
+
+
+def _cpu(*shape, dtype=None):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("bad,who", [
+    (dict(o=("f32",)), "o"),                         # fp32 O for bf16 inputs: the kernel would write bf16 offsets
+    (dict(k_blk=(1, 2, 16, 128)), "k_blk"),          # fewer block rows than queries
+    (dict(v_pre=(1, 2, 300, 64)), "v_pre"),          # head_dim disagrees
+    (dict(k_pre=(1, 3, 300, 128), v_pre=(1, 3, 300, 128)), "heads"),  # 8 q-heads over 3 kv-heads
+    (dict(idx=("i64",)), "idx"),                     # int64 indices
+    (dict(idx=("noncontig",)), "idx"),
+    (dict(lse=(1, 8, 31)), "lse"),
+])
+def test_binding_rejects_mismatched_arguments(bad, who):
+    """The C ABI takes pointers and one set of sizes; the binding checks every
+    tensor against them before anything reaches the library."""
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Bq, P, d = 1, 8, 2, 32, 300, 128
+    args = dict(q=_cpu(B, Hq, Bq, d), k_pre=_cpu(B, Hkv, P, d), v_pre=_cpu(B, Hkv, P, d),
+                k_blk=_cpu(B, Hkv, Bq, d), v_blk=_cpu(B, Hkv, Bq, d), o=_cpu(B, Hq, Bq, d),
+                lse=torch.zeros(B, Hq, Bq), idx=torch.zeros(B, Hkv, 50, dtype=torch.int32))
+    for k, v in bad.items():
+        if v == ("f32",):
+            args[k] = torch.zeros(*args[k].shape)
+        elif v == ("i64",):
+            args[k] = torch.zeros(B, Hkv, 50, dtype=torch.int64)
+        elif v == ("noncontig",):
+            args[k] = torch.zeros(B, Hkv, 100, dtype=torch.int32)[:, :, ::2]
+        elif k == "lse":
+            args[k] = torch.zeros(*v)
+        else:
+            args[k] = _cpu(*v)
+    with pytest.raises(ValueError, match=who):
+        ba.blkattn_full(args["q"], args["k_pre"], args["v_pre"], args["k_blk"], args["v_blk"], args["o"],
+                        args["lse"], idx=args["idx"])
+
+
+def test_binding_checks_partials_and_other_entry_points():
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Bq, P, d = 1, 4, 2, 32, 100, 64
+    q = _cpu(B, Hq, Bq, d)
+    kb = _cpu(B, Hkv, Bq, d)
+    good = ba.Partial(torch.zeros(B, Hq, Bq, d), torch.zeros(B, Hq, Bq), torch.zeros(B, Hq, Bq))
+    short = ba.Partial(torch.zeros(B, Hq, Bq - 1, d), torch.zeros(B, Hq, Bq - 1), torch.zeros(B, Hq, Bq - 1))
+    half = ba.Partial(good.o.to(torch.bfloat16), good.m, good.l)
+    with pytest.raises(ValueError, match="out.o"):
+        ba.blkattn_block_partial(q, kb, kb, short)
+    with pytest.raises(ValueError, match="out.o"):
+        ba.blkattn_prefix_partial(q, _cpu(B, Hkv, P, d), _cpu(B, Hkv, P, d), half)
+    with pytest.raises(ValueError, match="cached"):
+        ba.blkattn_block_step(q, kb, kb, short, _cpu(B, Hq, Bq, d))
+    with pytest.raises(ValueError, match="b.m"):
+        ba.blkattn_merge(good, ba.Partial(good.o, torch.zeros(B, Hq, Bq + 1), good.l), o=_cpu(B, Hq, Bq, d))
+    with pytest.raises(ValueError, match="k_out"):
+        ba.blkattn_gather_prefix(_cpu(B, Hkv, P, d), _cpu(B, Hkv, P, d), torch.zeros(B, Hkv, 10, dtype=torch.int32),
+                                 _cpu(B, Hkv, 9, d), _cpu(B, Hkv, 10, d))
+    with pytest.raises(ValueError, match="mass"):
+        ba.blkattn_prefix_mass(q, _cpu(B, Hkv, P, d), torch.zeros(B, Hq, Bq), torch.zeros(B, Hkv, P - 1))
+    with pytest.raises(ValueError, match="idx"):
+        ba.blkattn_select_retained(torch.zeros(B, Hkv, P), torch.zeros(B, Hkv, P + 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="cache"):
+        ba.blkattn_sequence_step(_cpu(B, Hq, P, d), _cpu(B, Hkv, P, d), _cpu(B, Hkv, P, d), 10, 32, short, True,
+                                 _cpu(B, Hq, P, d))
+    # consistent CPU arguments pass every shape check and stop at the device check
+    with pytest.raises(ValueError, match="GPU only"):
+        ba.blkattn_block_partial(q, kb, kb, good)

@@ -1,22 +1,32 @@
 """Throughput of block-diffusion attention over a cached prefix on one MI355X.
 
-Default workload (the metric's configuration): bf16, batch 4, 28 q-heads /
-4 kv-heads, head_dim 128, prefix P = 32768, block Bq = 32, 1 % of the prefix
-key rows scaled by 4; one step = one blkattn_full call (prefix partials over
-the key splits, the block tile, and the log-sum-exp merge). Inputs are
-generated on the host from fixed seeds, uploaded once and resident in HBM
-before timing; two copies are rotated so no step finds the previous step's
-K/V in the 256 MB Infinity Cache.
+Metric workload (the last JSON line): bf16, batch 4, 28 q-heads / 4 kv-heads,
+head_dim 128, prefix P = 32768, block Bq = 32, 1 % of the prefix key rows
+scaled by 4; one step = one blkattn_full call (the attention kernel over the
+key splits, then the log-sum-exp merge of the splits). Inputs are generated on
+the host from fixed seeds and uploaded once, resident in HBM before timing;
+two copies are rotated so that no step finds the previous step's K/V in the
+256 MB Infinity Cache.
 
-Prints one JSON line: throughput (algorithmic TFLOP/s over the whole step),
-the attention kernel's achieved HBM GB/s against the 8 TB/s peak (timed with
-HIP events around that kernel on its stream), and the fp64 CPU oracle timed on
-the same workload.
+Protocol of the metric line: a declared, time-based settle (back-to-back steps,
+untimed, so the clock has ramped up whatever --warmup is), W warmup steps, then
+K timed steps bracketed by a synchronize on both sides. In the same timed pass
+the attention kernel's own dispatch stamps a pair of HIP events around it
+(hipExtLaunchKernel), so its duration (kernel_ms, p10, p90) comes from the very
+steps whose average is ms_per_step; the run fails if kernel_ms > ms_per_step.
+Step p10/p90 come from the start-to-start intervals of those dispatches.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--path full|cached]
-  python bench.py --extra          # also one JSON line per secondary path
+Before the metric line, one JSON line per other workload (tiny fp32, LLaDA
+slice, reuse over 8 denoising steps, retained rows), each with its own roofline
+and CPU-oracle baseline. Workloads whose data fit in the Infinity Cache are
+timed launch by launch with a 512 MB write between launches (outside the timed
+kernel), so their GB/s are HBM figures.
+
+  python bench.py [--steps K] [--warmup W] [--settle S] [--no-configs] [--no-cpu-baseline]
+  python bench.py --extra          # large blocks and the full-sequence FACache step
   python bench.py --copy-probe     # plain device copy of known size (counter scale)
   python bench.py --record-traffic DIR   # write the traffic record from rocprofv3 runs
+  python bench.py --power SECONDS  # board power and clock while the step runs
 """
 
 from __future__ import annotations
@@ -39,10 +49,15 @@ METRIC = "cached-prefix block-attention TFLOP/s and HBM GB/s vs roofline at P=32
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_VALU_PEAK_TFLOPS = 157.3
+FLUSH_BYTES = 512 << 20
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def emit(d):
+    print(json.dumps(d), flush=True)
 
 
 def algorithmic(sh: datagen.Shape, with_block: bool = True):
@@ -58,23 +73,7 @@ def algorithmic(sh: datagen.Shape, with_block: bool = True):
     return dict(flops=flops, bytes=kv + q + out + idx,
                 # the attention kernel's own launch: K/V (+ indices) and Q in
                 kernel_bytes=kv + q + idx, units=B * Hkv,
-                unit_bytes=(kv + q + idx) / (B * Hkv))
-
-
-def measured_traffic(path, sh: datagen.Shape, fn_path: str):
-    """HBM bytes per attention-kernel launch from the committed counter record
-    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the record
-    is for another workload or the kernel sources changed since it was taken."""
-    if not path or not os.path.exists(path) or sh.name != "dream_gqa" or fn_path != "full":
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    srcs = rec.get("kernel_sources", [])
-    if not srcs or not all(os.path.exists(os.path.join(ROOT, x)) for x in srcs):
-        return None
-    if sources_sha256(srcs) != rec.get("kernel_sources_sha256"):
-        return None
-    return rec.get("bytes_per_launch")
+                unit_bytes=(kv + q + idx) / (B * Hkv), unit_flops=flops / (B * Hkv))
 
 
 def sources_sha256(paths) -> str:
@@ -87,43 +86,358 @@ def sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
+KERNEL_SOURCES = ("cached_block_attention_amd/csrc/attn_bf16.hip", "cached_block_attention_amd/csrc/gfx950.h",
+                  "cached_block_attention_amd/csrc/launch.h")
+
+
+def measured_traffic(path, sh: datagen.Shape):
+    """HBM bytes per attention-kernel launch from the committed counter record
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the record
+    is for another workload or the kernel sources changed since it was taken."""
+    if not path or not os.path.exists(path) or sh.name != "dream_gqa":
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    srcs = rec.get("kernel_sources", [])
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, x)) for x in srcs):
+        return None
+    if sources_sha256(srcs) != rec.get("kernel_sources_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def up(x, torch):
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def cpu_baseline(sh: datagen.Shape, inp, budget_s: float = 10.0):
-    """The fp64 oracle (as it stands) over the whole workload, repeated until
-    about `budget_s` seconds of CPU work; rate in the metric's unit."""
-    import oracle
+def upload(inp, torch):
+    d = {k: up(getattr(inp, k), torch) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
+    d["idx"] = up(inp.idx, torch) if inp.idx is not None else None
+    return d
+
+
+def oracle_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    flops = algorithmic(sh)["flops"]
+        return os.cpu_count() or 1
+
+
+def cpu_rate(fn, work: float, budget_s: float, unit: str, sample: str, scale_unit: float = 1e12):
+    """Time the fp64 oracle call fn() (as it stands) repeatedly for about
+    budget_s seconds; its rate is work per second in the given unit."""
     times = []
     t_all = time.perf_counter()
     while not times or (time.perf_counter() - t_all < budget_s and len(times) < 10):
         t0 = time.perf_counter()
-        oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=inp.idx)
+        fn()
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole {sh.name} workload (all {sh.batch * sh.q_heads} (batch, q-head) pairs), "
-                      f"{len(times)} passes, median {t:.2f} s per pass, numpy float64"}
+    return {"value": work / t / scale_unit, "unit": unit, "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{sample}; {len(times)} passes, median {t:.3f} s per pass, numpy float64"}
 
 
-KERNEL_SOURCES = ("cached_block_attention_amd/csrc/attn_bf16.hip", "cached_block_attention_amd/csrc/gfx950.h",
-                  "cached_block_attention_amd/csrc/launch.h")
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if len(xs) else None
 
+
+class Timer:
+    """Device timings on torch's current stream (where the library launches)."""
+
+    def __init__(self, torch, ba):
+        self.torch, self.ba = torch, ba
+        self.flush_buf = None
+
+    def events(self, n):
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:  # create the HIP events before anything is timed
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        return evs
+
+    def flush(self, i):
+        """Write 512 MB: evicts the 256 MB Infinity Cache and the L2s."""
+        if self.flush_buf is None:
+            self.flush_buf = self.torch.empty(FLUSH_BYTES, dtype=self.torch.uint8, device="cuda")
+        self.flush_buf.fill_(i & 0xFF)
+
+    def kernel_launches(self, launch, reps: int, flush: bool, hooked: bool):
+        """Per-launch device milliseconds of launch(i), i < reps: the attention
+        kernel's own dispatch-stamped events when hooked (the entry point hands
+        them to its attention launch), else events around the whole call; with
+        flush a 512 MB write precedes every launch (outside the timed span)."""
+        evs = self.events(reps)
+        for i, (a, b) in enumerate(evs):
+            if flush:
+                self.flush(i)
+            if hooked:
+                self.ba.set_kernel_events(a, b)
+                launch(i)
+            else:
+                a.record()
+                launch(i)
+                b.record()
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+
+def summary(ms):
+    return {"ms": round(float(np.median(ms)), 6), "ms_p10": round(pct(ms, 10), 6), "ms_p90": round(pct(ms, 90), 6)}
+
+
+def roofline(bound, work, ms, kernel, extra=None):
+    """Achieved rate of one kernel launch against MI355X's published peak."""
+    peak, unit = (HBM_PEAK_GBS, "GB/s") if bound == "hbm" else (BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")
+    if bound == "alu":
+        peak, unit = FP32_VALU_PEAK_TFLOPS, "TFLOP/s"
+    achieved = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    r = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": None, "kernel": kernel, "kernel_ms": round(ms, 6)}
+    if extra:
+        r.update(extra)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# the other workloads: one JSON line each
+# ---------------------------------------------------------------------------
+
+def config_lines(reps: int, with_cpu: bool, which):
+    import torch
+    import cached_block_attention_amd as ba
+    import oracle
+    tm = Timer(torch, ba)
+    reps = max(5, reps)
+
+    if "tiny_f32" in which:
+        sh = datagen.WORKLOADS["tiny_f32"]
+        inp = datagen.make_inputs(sh)
+        t = upload(inp, torch)
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(sh.batch, sh.q_heads, sh.block_len, dtype=torch.float32, device="cuda")
+        alg = algorithmic(sh)
+        call = lambda i: ba.blkattn_full(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], o, lse)
+        call(0)
+        ms = tm.kernel_launches(call, reps, flush=True, hooked=True)
+        s = summary(ms)
+        cpu = cpu_rate(lambda: oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale),
+                       alg["flops"], 2.0, "TFLOP/s", "the whole tiny_f32 workload") if with_cpu else None
+        emit({"config": "C1 tiny_f32: f32 B1 H4/4 d64 P256 Bq32", "function": "blkattn_full",
+              "kernel_ms": s["ms"], "kernel_ms_p10": s["ms_p10"], "kernel_ms_p90": s["ms_p90"],
+              "tflops": round(alg["flops"] / (s["ms"] * 1e-3) / 1e12, 4),
+              "note": "launch-latency bound (0.66 MB, 9.4 MFLOP); the target is parity only",
+              "roofline": roofline("hbm", alg["kernel_bytes"], s["ms"], "attn_f32_kernel",
+                                   {"algorithmic_bytes_per_launch": alg["kernel_bytes"], "flushed": True}),
+              "cpu_baseline": cpu})
+        del t, o, lse
+
+    if "llada_bf16" in which:
+        sh = datagen.WORKLOADS["llada_bf16"]
+        inp = datagen.make_inputs(sh)
+        t = upload(inp, torch)
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(sh.batch, sh.q_heads, sh.block_len, dtype=torch.float32, device="cuda")
+        dims = ba.make_dims(t["q"], sh.kv_heads, sh.prefix_len)
+        ws = torch.empty(max(16, ba.workspace_bytes(dims, ba.OP_FULL)), dtype=torch.uint8, device="cuda")
+        alg = algorithmic(sh)
+        call = lambda i: ba.blkattn_full(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], o, lse,
+                                         workspace=ws)
+        call(0)
+        kern = tm.kernel_launches(call, reps, flush=True, hooked=True)
+        whole = tm.kernel_launches(call, reps, flush=True, hooked=False)
+        sk, sw = summary(kern), summary(whole)
+        cpu = cpu_rate(lambda: oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale),
+                       alg["flops"], 3.0, "TFLOP/s", "the whole llada_bf16 workload") if with_cpu else None
+        emit({"config": "C2 llada_bf16: bf16 B1 H32/32 d128 P4096 Bq32", "function": "blkattn_full",
+              "splits": ba.plan_splits(dims, ba.OP_FULL),
+              "call_ms": sw["ms"], "call_ms_p10": sw["ms_p10"], "call_ms_p90": sw["ms_p90"],
+              "kernel_ms": sk["ms"], "kernel_ms_p10": sk["ms_p10"], "kernel_ms_p90": sk["ms_p90"],
+              "tflops_call": round(alg["flops"] / (sw["ms"] * 1e-3) / 1e12, 2),
+              "hbm_gbps_call": round(alg["bytes"] / (sw["ms"] * 1e-3) / 1e9, 1),
+              "roofline": roofline("hbm", alg["kernel_bytes"], sk["ms"], "attn_bf16_kernel",
+                                   {"algorithmic_bytes_per_launch": alg["kernel_bytes"], "flushed": True}),
+              "cpu_baseline": cpu})
+        del t, o, lse, ws
+
+    if "reuse_bf16" in which:
+        sh = datagen.WORKLOADS["reuse_bf16"]
+        log("generating reuse_bf16 inputs (2.15 GB prefix)")
+        inp = datagen.make_inputs(sh)
+        t = upload(inp, torch)
+        steps = [(t["q"], t["k_blk"], t["v_blk"])]
+        step_host = [(inp.q, inp.k_blk, inp.v_blk)]
+        for i in range(1, sh.steps):
+            qn, kn, vn = datagen.step_inputs(sh, i)
+            step_host.append((qn, kn, vn))
+            steps.append((up(qn, torch), up(kn, torch), up(vn, torch)))
+        B, Hq, Bq, d = sh.batch, sh.q_heads, sh.block_len, sh.head_dim
+        pp = ba.empty_partial(B, Hq, Bq, d, "cuda")
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device="cuda")
+        dims = ba.make_dims(t["q"], sh.kv_heads, sh.prefix_len)
+        ws = torch.empty(max(16, ba.workspace_bytes(dims, ba.OP_PREFIX_PARTIAL),
+                             ba.workspace_bytes(dims, ba.OP_FULL)), dtype=torch.uint8, device="cuda")
+        pre = lambda i: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp, workspace=ws)
+        pre(0)
+        n_pre = max(5, reps // 4)
+        kern = summary(tm.kernel_launches(pre, n_pre, flush=False, hooked=True))
+        call_pre = summary(tm.kernel_launches(pre, n_pre, flush=False, hooked=False))
+        stepf = lambda i: ba.blkattn_block_step(*steps[i % sh.steps], pp, o, lse)
+        stepf(0)
+        st = summary(tm.kernel_launches(stepf, max(reps, 2 * sh.steps), flush=True, hooked=False))
+        recompute = lambda i: ba.blkattn_full(steps[i % sh.steps][0], t["k_pre"], t["v_pre"], steps[i % sh.steps][1],
+                                              steps[i % sh.steps][2], o, lse, workspace=ws)
+        recompute(1)
+        rec = summary(tm.kernel_launches(recompute, n_pre, flush=False, hooked=False))
+        alg_pre = algorithmic(sh, with_block=False)
+        n = sh.steps
+        amort = (call_pre["ms"] + n * st["ms"]) / n
+        # a step reads q, k_blk, v_blk and the cached (o, m, l); writes O and LSE
+        step_bytes = 2.0 * B * Hq * Bq * d * 2 + 2 * 2.0 * B * sh.kv_heads * Bq * d + 4.0 * B * Hq * Bq * (d + 2) \
+            + 4.0 * B * Hq * Bq
+        cpu = None
+        if with_cpu:
+            # the prefix partial of two (batch, kv-head) pairs, scaled to the rate
+            qs, ks, vs = inp.q[:1, :2], inp.k_pre[:1, :2], inp.v_pre[:1, :2]
+            cpu = cpu_rate(lambda: oracle.partial(qs, ks, vs, sh.scale), 4.0 * 2 * Bq * sh.prefix_len * d, 4.0,
+                           "TFLOP/s", "prefix partial of 2 of the 256 (batch, head) pairs (P 16384)")
+        emit({"config": "C4 reuse_bf16: bf16 B8 H32/32 d128 P16384 Bq32, 8 denoising steps",
+              "function": "blkattn_prefix_partial once, then blkattn_block_step per step",
+              "prefix_partial_call_ms": call_pre["ms"], "prefix_partial_kernel_ms": kern["ms"],
+              "prefix_partial_kernel_ms_p10": kern["ms_p10"], "prefix_partial_kernel_ms_p90": kern["ms_p90"],
+              "block_step_ms": st["ms"], "block_step_ms_p10": st["ms_p10"], "block_step_ms_p90": st["ms_p90"],
+              "block_step_hbm_gbps": round(step_bytes / (st["ms"] * 1e-3) / 1e9, 1),
+              "full_recompute_ms": rec["ms"], "amortized_ms_per_step": round(amort, 6),
+              "reuse_gain_vs_recompute": round(rec["ms"] / amort, 2),
+              "roofline": roofline("hbm", alg_pre["kernel_bytes"], kern["ms"], "attn_bf16_kernel (prefix partial)",
+                                   {"algorithmic_bytes_per_launch": alg_pre["kernel_bytes"], "flushed": False,
+                                    "note": "2.15 GB of K/V per launch is 8x the Infinity Cache"}),
+              "cpu_baseline": cpu})
+        del t, steps, pp, o, lse, ws, inp
+        torch.cuda.empty_cache()
+
+    if "sparse_gqa" in which:
+        sh = datagen.WORKLOADS["sparse_gqa"]
+        log("generating sparse_gqa inputs")
+        inp = datagen.make_inputs(sh)
+        t = upload(inp, torch)
+        B, Hq, Hkv, Bq, d, P, nk = (sh.batch, sh.q_heads, sh.kv_heads, sh.block_len, sh.head_dim, sh.prefix_len,
+                                    sh.n_keep)
+        G = Hq // Hkv
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device="cuda")
+        dims = ba.make_dims(t["q"], Hkv, P, nk)
+        ws = torch.empty(max(16, ba.workspace_bytes(dims, ba.OP_FULL)), dtype=torch.uint8, device="cuda")
+        fused = lambda i: ba.blkattn_full(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], o, lse,
+                                          idx=t["idx"], workspace=ws)
+        fused(0)
+        kern = summary(tm.kernel_launches(fused, reps, flush=True, hooked=True))
+        call = summary(tm.kernel_launches(fused, reps, flush=True, hooked=False))
+        ko = torch.empty(B, Hkv, nk, d, dtype=t["k_pre"].dtype, device="cuda")
+        vo = torch.empty_like(ko)
+        gat = lambda i: ba.blkattn_gather_prefix(t["k_pre"], t["v_pre"], t["idx"], ko, vo)
+        gat(0)
+        g = summary(tm.kernel_launches(gat, reps, flush=True, hooked=False))
+        _, lse_all = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
+        mass = torch.empty(B, Hkv, P, dtype=torch.float32, device="cuda")
+        massf = lambda i: ba.blkattn_prefix_mass(t["q"], t["k_pre"], lse_all, mass)
+        massf(0)
+        m = summary(tm.kernel_launches(massf, reps, flush=True, hooked=False))
+        idx = torch.empty(B, Hkv, nk, dtype=torch.int32, device="cuda")
+        sel_dims = ba.Dims(B, Hkv, Hkv, 64, 1, nk, P, ba.F32, 1.0, 0, 0)
+        sel_ws = torch.empty(ba.workspace_bytes(sel_dims, ba.OP_SELECT), dtype=torch.uint8, device="cuda")
+        self_ = lambda i: ba.blkattn_select_retained(mass, idx, workspace=sel_ws)
+        self_(0)
+        se = summary(tm.kernel_launches(self_, reps, flush=True, hooked=False))
+        alg = algorithmic(sh)
+        mass_flops = 2.0 * B * Hkv * G * Bq * P * d
+        gather_bytes = 2 * 2.0 * 2 * B * Hkv * nk * d
+        cpu = None
+        if with_cpu:
+            cpu = cpu_rate(lambda: oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale,
+                                               idx=inp.idx), alg["flops"], 5.0, "TFLOP/s",
+                           "the whole sparse_gqa fused-gather attention")
+        emit({"config": "C5 sparse_gqa: bf16 B2 Hq28/Hkv4 d128 P_full131072 keep8192 Bq64",
+              "function": "blkattn_full with idx (fused gather)",
+              "call_ms": call["ms"], "kernel_ms": kern["ms"], "kernel_ms_p10": kern["ms_p10"],
+              "kernel_ms_p90": kern["ms_p90"], "tflops_call": round(alg["flops"] / (call["ms"] * 1e-3) / 1e12, 1),
+              "gather_ms": g["ms"], "gather_hbm_gbps": round(gather_bytes / (g["ms"] * 1e-3) / 1e9, 1),
+              "mass_ms": m["ms"], "mass_tflops": round(mass_flops / (m["ms"] * 1e-3) / 1e12, 1),
+              "select_ms": se["ms"],
+              "roofline": roofline("mfma", alg["flops"], kern["ms"], "attn_bf16_pp_kernel (fused gather)",
+                                   {"algorithmic_flops_per_launch": alg["flops"], "flushed": True}),
+              "cpu_baseline": cpu})
+        del t, o, lse, ws, ko, vo, mass, idx, sel_ws, lse_all, inp
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# secondary paths not covered by the config lines (--extra)
+# ---------------------------------------------------------------------------
+
+def extra_lines(reps: int):
+    """Large blocks (block partial) and the full-sequence FACache step."""
+    import torch
+    import cached_block_attention_amd as ba
+    tm = Timer(torch, ba)
+    for bq in (256, 1024):
+        sh = datagen.scaled_shape("llada_bf16", block_len=bq, prefix_len=0)
+        t = upload(datagen.make_inputs(sh), torch)
+        pbq = ba.empty_partial(sh.batch, sh.q_heads, bq, sh.head_dim, "cuda")
+        f = lambda i: ba.blkattn_block_partial(t["q"], t["k_blk"], t["v_blk"], pbq)
+        f(0)
+        s = summary(tm.kernel_launches(f, reps, flush=True, hooked=False))
+        fl = 4.0 * sh.batch * sh.q_heads * bq * bq * sh.head_dim
+        emit({"path": "blkattn_block_partial", "workload": f"large block Bq{bq} B1 H32 d128", **s,
+              "tflops": round(fl / s["ms"] / 1e9, 1), "mfma_frac": round(fl / s["ms"] / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4)})
+        del t, pbq
+    sh = datagen.WORKLOADS["llada_seq"]
+    B, Hq, N, d, Bq, c0 = sh.batch, sh.q_heads, sh.prefix_len, sh.head_dim, sh.block_len, sh.block_start
+    q, k, v = (up(x, torch) for x in datagen.sequence_inputs(sh, 0))
+    cache = ba.empty_partial(B, Hq, N, d, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
+    dims = ba.Dims(B, Hq, sh.kv_heads, d, Bq, 0, N, ba.BF16, float(sh.scale), 0, 0)
+    ws = torch.empty(max(16, ba.workspace_bytes(dims, ba.OP_SEQUENCE)), dtype=torch.uint8, device="cuda")
+    gen = lambda i: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, True, o, lse, workspace=ws)
+    reuse = lambda i: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, False, o, lse, workspace=ws)
+    gen(0)
+    sg = summary(tm.kernel_launches(gen, reps, flush=True, hooked=False))
+    sr = summary(tm.kernel_launches(reuse, reps, flush=True, hooked=False))
+    full = ba.empty_partial(B, Hq, N, d, "cuda")
+    allrows = lambda i: ba.blkattn_prefix_partial(q, k, v, full)
+    allrows(0)
+    sf = summary(tm.kernel_launches(allrows, reps, flush=True, hooked=False))
+    nu = N - Bq
+    fl_gen = 4.0 * B * Hq * (nu * nu + nu * Bq + Bq * N) * d
+    fl_step = 4.0 * B * Hq * (nu * Bq + Bq * N) * d
+    fl_full = 4.0 * B * Hq * N * N * d
+    step_bytes = (2.0 * B * Hq * N * d + 4.0 * B * Hq * nu * (d + 2) + 2 * 2.0 * B * sh.kv_heads * N * d
+                  + 2.0 * B * Hq * N * d + 4.0 * B * Hq * N)
+    n = sh.steps
+    amort = (sg["ms"] + (n - 1) * sr["ms"]) / n
+    emit({"path": "blkattn_sequence_step", "workload": f"llada_seq B1 H32 d128 N{N} block [{c0},{c0 + Bq}), {n} steps",
+          "first_step_ms": sg["ms"], "first_step_tflops": round(fl_gen / sg["ms"] / 1e9, 1),
+          "reuse_step_ms": sr["ms"], "reuse_step_hbm_gbps": round(step_bytes / sr["ms"] / 1e6, 1),
+          "reuse_step_tflops": round(fl_step / sr["ms"] / 1e9, 1),
+          "full_attention_ms": sf["ms"], "full_attention_tflops": round(fl_full / sf["ms"] / 1e9, 1),
+          "amortized_ms_per_step": round(amort, 5), "facache_gain": round(sf["ms"] / amort, 2)})
+
+
+# ---------------------------------------------------------------------------
+# counters, copy probe, power
+# ---------------------------------------------------------------------------
 
 def attention_kernel_name(sh: datagen.Shape) -> str:
     """Name of the attention kernel a blkattn_full call of this workload runs:
-    eight-wave workgroups with at most 224 packed rows (129 to 224 rows per
-    kv-head chunk) run the ping-pong kernel with its dedicated DMA wave, fp32
-    workloads the fp32 kernel, everything else the sequential bf16 kernel."""
+    eight-wave workgroups with at most 224 packed rows run the ping-pong
+    kernel, fp32 workloads the fp32 kernel, everything else the sequential
+    bf16 kernel."""
     if sh.dtype != datagen.BF16:
         return "attn_f32_kernel"
     rows = sh.q_heads // sh.kv_heads * sh.block_len
@@ -135,9 +449,10 @@ def attention_kernel_name(sh: datagen.Shape) -> str:
 def record_traffic(top: str, out_path: str):
     """Traffic record of the metric workload's attention kernel from four
     rocprofv3 counter runs under `top`: pmc_fetch / pmc_write (FETCH_SIZE /
-    WRITE_SIZE of `bench.py --steps 5 --warmup 2 --no-cpu-baseline`) and
-    pmc_cfetch / pmc_cwrite (the same counters over `bench.py --copy-probe`).
-    The copy moves a known number of bytes, which gives each counter's scale."""
+    WRITE_SIZE of `bench.py --steps 5 --warmup 2 --settle 0 --no-configs
+    --no-cpu-baseline`) and pmc_cfetch / pmc_cwrite (the same counters over
+    `bench.py --copy-probe`). The copy moves a known number of bytes, which gives
+    each counter's scale."""
     import csv
     import glob
 
@@ -163,6 +478,7 @@ def record_traffic(top: str, out_path: str):
     write_scale = copy_bytes / (cw * 1024.0)
     f = per_dispatch("pmc_fetch", kern)
     w = per_dispatch("pmc_write", kern)
+    cmd = "python3 bench.py --steps 5 --warmup 2 --settle 0 --no-configs --no-cpu-baseline"
     rec = {
         "kernel": kern,
         "workload": "dream_gqa: bf16 B4 Hq28/Hkv4 d128 P32768 Bq32, 16 key splits",
@@ -174,8 +490,8 @@ def record_traffic(top: str, out_path: str):
                        "fetch_scale": fetch_scale, "write_scale": write_scale},
         "bytes_per_launch": int(round(f * 1024.0 * fetch_scale + w * 1024.0 * write_scale)),
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- {cmd}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- {cmd}",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- python3 bench.py --copy-probe",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o run -- python3 bench.py --copy-probe",
         ],
@@ -198,175 +514,25 @@ def copy_probe(mib: int = 1024):
     print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}))
 
 
-def _median_ms(fn, reps: int, warm: int = 3):
-    """Median device time (ms) of fn() over `reps` calls, HIP events around each."""
-    import torch
-    for _ in range(warm):
-        fn()
+def copy_gbps(torch, mib: int = 1024, reps: int = 10) -> float:
+    """Measured device-copy bandwidth (bytes read + written per second): the
+    empirical HBM ceiling, a second denominator beside the published peak."""
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
     torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in evs]))
-
-
-EXTRA_PATHS = ("prefix", "llada", "reuse", "retention", "large", "sequence")
-
-
-def extra_lines(reps: int, paths=EXTRA_PATHS):
-    """Timings of the other paths (one JSON line each): the prefix partial at the
-    metric workload, dense attention at the LLaDA slice, the reuse path over 8
-    steps, the retained-row pipeline at the sparse workload, large blocks and the
-    full-sequence FACache step; `paths` picks a subset."""
-    import torch
-    import cached_block_attention_amd as ba
-
-    def emit(**kw):
-        print(json.dumps(kw), flush=True)
-
-    def upl(inp):
-        d = {k: up(getattr(inp, k), torch) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
-        d["idx"] = up(inp.idx, torch) if inp.idx is not None else None
-        return d
-
-    if "prefix" in paths:
-        # prefix partial at the metric workload (the state FACache stores)
-        sh = datagen.WORKLOADS["dream_gqa"]
-        t = upl(datagen.make_inputs(sh))
-        alg = algorithmic(sh, with_block=False)
-        pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-        ms = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), reps)
-        emit(path="blkattn_prefix_partial", workload="dream_gqa P32768", ms=round(ms, 4),
-             tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
-        del t, pp
-        torch.cuda.empty_cache()
-
-    if "llada" in paths:
-        # dense attention at the LLaDA slice (fits the 256 MB MALL: timed as is)
-        sh = datagen.WORKLOADS["llada_bf16"]
-        t = upl(datagen.make_inputs(sh))
-        alg = algorithmic(sh)
-        ms = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"]), reps)
-        emit(path="blkattn_full", workload="llada_bf16 P4096", ms=round(ms, 4),
-             tflops=round(alg["flops"] / ms / 1e9, 1), hbm_gbps=round(alg["bytes"] / ms / 1e6, 1))
-        del t
-        torch.cuda.empty_cache()
-
-    if "reuse" in paths:
-        # reuse over 8 denoising steps: prefix partial once, then per step the fused
-        # block step, or block partial + merge, against recomputing full attention
-        sh = datagen.WORKLOADS["reuse_bf16"]
-        inp = datagen.make_inputs(sh)
-        t = upl(inp)
-        steps = [(t["q"], t["k_blk"], t["v_blk"])]
-        for i in range(1, sh.steps):
-            qn, kn, vn = datagen.step_inputs(sh, i)
-            steps.append((up(qn, torch), up(kn, torch), up(vn, torch)))
-        pp = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-        o = torch.empty_like(t["q"])
-        lse = torch.empty(sh.batch, sh.q_heads, sh.block_len, dtype=torch.float32, device="cuda")
-        pb = ba.empty_partial(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, "cuda")
-        ms_prefix = _median_ms(lambda: ba.blkattn_prefix_partial(t["q"], t["k_pre"], t["v_pre"], pp), max(3, reps // 10))
-        ms_step = float(np.median([_median_ms(lambda s=s: ba.blkattn_block_step(s[0], s[1], s[2], pp, o, lse), reps)
-                                   for s in steps]))
-        def two_launch(s):
-            ba.blkattn_block_partial(s[0], s[1], s[2], pb)
-            ba.blkattn_merge(pp, pb, o=o, lse=lse)
-        ms_two = float(np.median([_median_ms(lambda s=s: two_launch(s), reps) for s in steps]))
-        wsf = torch.empty(ba.workspace_bytes(ba.make_dims(t["q"], sh.kv_heads, sh.prefix_len), ba.OP_FULL) + 16,
-                          dtype=torch.uint8, device="cuda")
-        ms_full = _median_ms(lambda: ba.blkattn_full(steps[1][0], t["k_pre"], t["v_pre"], steps[1][1], steps[1][2], o, lse,
-                                                     workspace=wsf), max(3, reps // 10))
-        n = sh.steps
-        emit(path="reuse", workload=f"reuse_bf16 B8 H32 P16384 Bq32, {n} steps", prefix_partial_ms=round(ms_prefix, 4),
-             block_step_ms=round(ms_step, 4), block_partial_plus_merge_ms=round(ms_two, 4),
-             full_recompute_ms=round(ms_full, 4),
-             amortized_ms_per_step=round((ms_prefix + n * ms_step) / n, 4),
-             reuse_gain=round(ms_full / ((ms_prefix + n * ms_step) / n), 2),
-             prefix_partial_hbm_gbps=round(algorithmic(sh, with_block=False)["bytes"] / ms_prefix / 1e6, 1))
-        del t, steps, pp, pb, inp
-        torch.cuda.empty_cache()
-
-    if "retention" in paths:
-        # retained rows at the sparse workload: mass over all 131072 rows, top-k,
-        # standalone gather, and the fused-gather attention over the kept rows
-        sh = datagen.WORKLOADS["sparse_gqa"]
-        inp = datagen.make_inputs(sh)
-        t = upl(inp)
-        _, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"])
-        mass = torch.empty(sh.batch, sh.kv_heads, sh.prefix_len, dtype=torch.float32, device="cuda")
-        idx = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, dtype=torch.int32, device="cuda")
-        ms_mass = _median_ms(lambda: ba.blkattn_prefix_mass(t["q"], t["k_pre"], lse, mass), reps)
-        sel_dims = ba.Dims(sh.batch, sh.kv_heads, sh.kv_heads, 64, 1, sh.n_keep, sh.prefix_len, ba.F32, 1.0, 0, 0)
-        sel_ws = torch.empty(ba.workspace_bytes(sel_dims, ba.OP_SELECT), dtype=torch.uint8, device="cuda")
-        ms_sel = _median_ms(lambda: ba.blkattn_select_retained(mass, idx, workspace=sel_ws), reps)
-        ko = torch.empty(sh.batch, sh.kv_heads, sh.n_keep, sh.head_dim, dtype=t["k_pre"].dtype, device="cuda")
-        vo = torch.empty_like(ko)
-        ms_gather = _median_ms(lambda: ba.blkattn_gather_prefix(t["k_pre"], t["v_pre"], t["idx"], ko, vo), reps)
-        ms_fused = _median_ms(lambda: ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"]), reps)
-        G = sh.q_heads // sh.kv_heads
-        mass_flops = 2.0 * sh.batch * sh.kv_heads * G * sh.block_len * sh.prefix_len * sh.head_dim
-        mass_bytes = 2.0 * sh.batch * sh.kv_heads * sh.prefix_len * sh.head_dim + 4.0 * sh.batch * sh.kv_heads * sh.prefix_len
-        alg = algorithmic(sh)
-        gather_bytes = 2 * 2.0 * 2 * sh.batch * sh.kv_heads * sh.n_keep * sh.head_dim
-        emit(path="retention", workload="sparse_gqa B2 Hq28/Hkv4 P_full131072 keep8192 Bq64",
-             mass_ms=round(ms_mass, 4), mass_tflops=round(mass_flops / ms_mass / 1e9, 1),
-             mass_hbm_gbps=round(mass_bytes / ms_mass / 1e6, 1), select_ms=round(ms_sel, 4),
-             gather_ms=round(ms_gather, 4), gather_gbps=round(gather_bytes / ms_gather / 1e6, 1),
-             fused_gather_full_ms=round(ms_fused, 4), fused_tflops=round(alg["flops"] / ms_fused / 1e9, 1))
-        del t, inp, mass, idx, ko, vo
-        torch.cuda.empty_cache()
-
-    if "large" in paths:
-        # a large block (square, compute-bound bidirectional tile): block partial
-        for bq in (256, 1024):
-            sh = datagen.scaled_shape("llada_bf16", block_len=bq, prefix_len=0)
-            t = upl(datagen.make_inputs(sh))
-            pbq = ba.empty_partial(sh.batch, sh.q_heads, bq, sh.head_dim, "cuda")
-            ms = _median_ms(lambda: ba.blkattn_block_partial(t["q"], t["k_blk"], t["v_blk"], pbq), reps)
-            fl = 4.0 * sh.batch * sh.q_heads * bq * bq * sh.head_dim
-            emit(path="blkattn_block_partial", workload=f"large block Bq{bq} B1 H32 d128", ms=round(ms, 4),
-                 tflops=round(fl / ms / 1e9, 1), mfma_frac=round(fl / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
-            del t, pbq
-            torch.cuda.empty_cache()
-
-    if "sequence" in paths:
-        # full-sequence FACache step (LLaDA-like: 4096 rows, block at rows 2048..2079):
-        # the block's first step builds the cache, later steps reuse it; against
-        # plain attention of every row over every row at each step
-        sh = datagen.WORKLOADS["llada_seq"]
-        B, Hq, N, d, Bq, c0 = sh.batch, sh.q_heads, sh.prefix_len, sh.head_dim, sh.block_len, sh.block_start
-        q, k, v = (up(x, torch) for x in datagen.sequence_inputs(sh, 0))
-        cache = ba.empty_partial(B, Hq, N, d, "cuda")
-        o = torch.empty_like(q)
-        lse = torch.empty(B, Hq, N, dtype=torch.float32, device="cuda")
-        dims = ba.Dims(B, Hq, sh.kv_heads, d, Bq, 0, N, ba.BF16, float(sh.scale), 0, 0)
-        ws = torch.empty(max(1, ba.workspace_bytes(dims, ba.OP_SEQUENCE)), dtype=torch.uint8, device="cuda")
-        ms_gen = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, True, o, lse, workspace=ws), reps)
-        ms_step = _median_ms(lambda: ba.blkattn_sequence_step(q, k, v, c0, Bq, cache, False, o, lse, workspace=ws), reps)
-        full = ba.empty_partial(B, Hq, N, d, "cuda")
-        ms_full = _median_ms(lambda: ba.blkattn_prefix_partial(q, k, v, full), reps)
-        nu = N - Bq
-        fl_gen = 4.0 * B * Hq * (nu * nu + nu * Bq + Bq * N) * d
-        fl_step = 4.0 * B * Hq * (nu * Bq + Bq * N) * d
-        fl_full = 4.0 * B * Hq * N * N * d
-        # a reuse step reads q, the cached (o, m, l) of the other rows and the whole
-        # sequence's k, v (for the block queries), and writes o and lse
-        step_bytes = (2.0 * B * Hq * N * d + 4.0 * B * Hq * nu * (d + 2) + 2 * 2.0 * B * sh.kv_heads * N * d
-                      + 2.0 * B * Hq * N * d + 4.0 * B * Hq * N)
-        n = sh.steps
-        amort = (ms_gen + (n - 1) * ms_step) / n
-        emit(path="blkattn_sequence_step", workload=f"llada_seq B1 H32 d128 N{N} block [{c0},{c0 + Bq}), {n} steps",
-             first_step_ms=round(ms_gen, 4), first_step_tflops=round(fl_gen / ms_gen / 1e9, 1),
-             reuse_step_ms=round(ms_step, 4), reuse_step_tflops=round(fl_step / ms_step / 1e9, 1),
-             reuse_step_hbm_gbps=round(step_bytes / ms_step / 1e6, 1),
-             full_attention_ms=round(ms_full, 4), full_attention_tflops=round(fl_full / ms_full / 1e9, 1),
-             amortized_ms_per_step=round(amort, 4), facache_gain=round(ms_full / amort, 2))
-        del q, k, v, cache, o, lse, ws, full
-        torch.cuda.empty_cache()
+    gbps = 2.0 * n * 4 * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
 
 
 def power_line(step, seconds: float, sh: datagen.Shape):
@@ -420,29 +586,35 @@ def power_line(step, seconds: float, sh: datagen.Shape):
     }), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# the metric line
+# ---------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400,
-                    help="untimed steps first; the GPU clock needs some 300 back-to-back calls to ramp up "
-                         "from idle, so the timed steps see the steady state")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=1.5, metavar="SECONDS",
+                    help="untimed back-to-back steps for this long before the warmup, so the clock has "
+                         "ramped up from idle whatever --warmup is")
     ap.add_argument("--workload", default="dream_gqa",
                     choices=sorted(k for k, w in datagen.WORKLOADS.items() if w.block_start is None))
     ap.add_argument("--path", default="full", choices=["full", "cached"],
                     help="full: blkattn_full; cached: prefix partial + block partial + merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="print only the metric line (no lines for the other workloads)")
+    ap.add_argument("--configs", default="tiny_f32,llada_bf16,reuse_bf16,sparse_gqa",
+                    help="comma-separated other workloads to print a line for before the metric line")
     ap.add_argument("--power", type=float, metavar="SECONDS",
                     help="after the warmup, run the step back to back for SECONDS while sampling board power "
                          "and clocks with amd-smi; print one JSON line and exit")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="write the --traffic record from the four rocprofv3 counter runs under DIR")
-    ap.add_argument("--extra-path", choices=EXTRA_PATHS, action="append",
-                    help="with --extra: only this secondary path (repeatable)")
     ap.add_argument("--extra", action="store_true",
-                    help="time the other paths (prefix partial, LLaDA slice, reuse steps, retention, "
-                         "large blocks, full-sequence step) instead of the metric line")
+                    help="time large blocks and the full-sequence FACache step instead of the metric line")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "attn_bf16_dream_gqa_traffic.json"),
                     help="JSON record of the attention kernel's measured HBM bytes per launch "
                          "(used only while its kernel-source hash matches the current source)")
@@ -461,26 +633,26 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    if args.extra:
-        extra_lines(max(10, args.steps // 10), tuple(args.extra_path or EXTRA_PATHS))
-        return
     import cached_block_attention_amd as ba
-    ba.library()
+    ba.library()   # raises when the HIP library is missing: there is no other path
+    if args.extra:
+        extra_lines(max(10, min(args.steps, 50)))
+        return
+
+    with_cpu = not args.no_cpu_baseline
+    if not args.no_configs and not args.power:
+        which = [w for w in args.configs.split(",") if w]
+        config_lines(min(args.steps, 20), with_cpu, which)
 
     sh = datagen.WORKLOADS[args.workload]
     log(f"generating {sh.name} inputs")
     inp = datagen.make_inputs(sh)
-    copies = []
-    for c in range(2):
-        d = {k: up(getattr(inp, k), torch) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
-        d["idx"] = up(inp.idx, torch) if inp.idx is not None else None
-        copies.append(d)
+    copies = [upload(inp, torch) for _ in range(2)]
     B, Hq, Bq, dh = inp.q.shape
     dtype = copies[0]["q"].dtype
     o = torch.empty(B, Hq, Bq, dh, dtype=dtype, device="cuda")
     lse = torch.empty(B, Hq, Bq, dtype=torch.float32, device="cuda")
-    dims = ba.make_dims(copies[0]["q"], sh.kv_heads, sh.prefix_len,
-                        sh.n_keep or 0)
+    dims = ba.make_dims(copies[0]["q"], sh.kv_heads, sh.prefix_len, sh.n_keep or 0)
     ws = torch.empty(max(ba.workspace_bytes(dims, ba.OP_FULL),
                          ba.workspace_bytes(dims, ba.OP_PREFIX_PARTIAL), 16),
                      dtype=torch.uint8, device="cuda")
@@ -500,7 +672,15 @@ def main():
             ba.blkattn_block_partial(t["q"], t["k_blk"], t["v_blk"], pb)
             ba.blkattn_merge(pp, pb, o=o, lse=lse)
 
-    log(f"warmup {args.warmup} steps")
+    copy_bw = copy_gbps(torch)
+    log(f"settle {args.settle} s, then warmup {args.warmup} steps")
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < args.settle:
+        for _ in range(50):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -508,55 +688,53 @@ def main():
         power_line(step, args.power, sh)
         return
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:   # create the HIP events before the timed region
-        a.record()
-        b.record()
+    K = args.steps
+    tm = Timer(torch, ba)
+    evs = tm.events(K)
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    # The K timed steps run exactly as a caller runs them. Events around
-    # every attention launch would stretch each step (the stream waits on
-    # them between kernels), so the kernel's own duration comes from a second
-    # pass of K steps with per-launch events.
-    log(f"timing {args.steps} steps")
+    # The K timed steps: each attention launch carries its own dispatch-stamped
+    # begin/end events (no extra packets between the steps' kernels).
+    log(f"timing {K} steps")
     wall0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_stop) / args.steps
-    log(f"timing the attention kernel over {args.steps} more steps")
-    t_start.record()
-    for i in range(args.steps):
+    for i in range(K):
         step(i, evs[i])
     t_stop.record()
     torch.cuda.synchronize()
-    ms_step_ev = t_start.elapsed_time(t_stop) / args.steps
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_stop) / K
+    k_ms_all = [a.elapsed_time(b) for a, b in evs]
+    k_ms = float(np.mean(k_ms_all))
+    intervals = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(K - 1)]
+    if k_ms > ms_step:
+        raise SystemExit(f"inconsistent timing: attention kernel {k_ms:.6f} ms > step {ms_step:.6f} ms")
 
     alg = algorithmic(sh, with_block=(args.path == "full"))
     full_alg = algorithmic(sh)
     tflops = full_alg["flops"] / (ms_step * 1e-3) / 1e12
     achieved = alg["kernel_bytes"] / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.traffic, sh, args.path)
+    traffic = measured_traffic(args.traffic, sh) if args.path == "full" else None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         log("timing the fp64 oracle on the host")
-        cpu = cpu_baseline(sh, inp)
+        cpu = cpu_rate(lambda: oracle_full(inp, sh), full_alg["flops"], 10.0, "TFLOP/s",
+                       f"the whole {sh.name} workload (all {sh.batch * sh.q_heads} (batch, q-head) pairs)")
 
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
+        "settle_s": args.settle,
+        "settle_steps": n_settle,
         "ms_per_step": round(ms_step, 6),
+        "step_ms_p10": round(pct(intervals, 10), 6) if intervals else None,
+        "step_ms_p90": round(pct(intervals, 90), 6) if intervals else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -583,14 +761,24 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel_ms": round(k_ms, 6),
-            "kernel_ms_from": f"HIP events of each attention launch over a second pass of {args.steps} steps "
-                              f"({ms_step_ev:.6f} ms per step with the events)",
+            "kernel_ms_p10": round(pct(k_ms_all, 10), 6),
+            "kernel_ms_p90": round(pct(k_ms_all, 90), 6),
+            "kernel_ms_from": "the attention kernel's dispatch-stamped HIP events in each of the timed steps",
+            "mfma_frac_kernel": round(full_alg["flops"] / (k_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "algorithmic_bytes_per_launch": alg["kernel_bytes"],
+            "units": alg["units"], "unit_bytes": alg["unit_bytes"],
+            "copy_gbps_measured": round(copy_bw, 1),
+            "frac_of_copy": round(achieved / copy_bw, 4),
         },
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
+
+
+def oracle_full(inp, sh):
+    import oracle
+    return oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=inp.idx)
 
 
 if __name__ == "__main__":

@@ -156,10 +156,10 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (p.head_dim == 128) {
     const int64_t blocks = (rows + 7) / 8;
-    hipLaunchKernelGGL((merge_kernel<128, 8>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else if (p.head_dim == 64) {
     const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL((merge_kernel<64, 8>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -97,6 +97,7 @@ def library() -> ctypes.CDLL:
     pd, pt, pp = _P(Dims), _P(Tensor), _P(PartialDesc)
     sig = {
         "blkattn_full": (ctypes.c_int, [pd, pt, pt, pt, vp, pt, pt, pt, vp, vp, sz, vp]),
+        "blkattn_full_noalloc": (ctypes.c_int, [pd, pt, pt, pt, vp, pt, pt, pt, vp, vp]),
         "blkattn_prefix_partial": (ctypes.c_int, [pd, pt, pt, pt, vp, pp, vp, sz, vp]),
         "blkattn_block_partial": (ctypes.c_int, [pd, pt, pt, pt, pp, vp]),
         "blkattn_block_step": (ctypes.c_int, [pd, pt, pt, pt, pp, pt, vp, vp]),
@@ -318,6 +319,27 @@ def blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=Non
                                 _ref(_tensor(v_pre)), _ptr(idx), _ref(_tensor(k_blk)),
                                 _ref(_tensor(v_blk)), _ref(_tensor(o)), _ptr(lse), _ptr(ws),
                                 nbytes, _stream(stream))
+    _raise(st)
+    return o, lse
+
+
+def blkattn_full_noalloc(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=None, splits=0,
+                         stream=None):
+    """blkattn_full with the key-split scratch in the library's static device
+    array (no allocation, no workspace argument; see include/blkattn.h)."""
+    torch = _torch()
+    B, Hq, Hkv, d = _check_qkv(q, k_pre, v_pre, "k_pre", "v_pre")
+    Bq = q.shape[2]
+    _expect(k_blk, "k_blk", (B, Hkv, Bq, d), q.dtype)
+    _expect(v_blk, "v_blk", (B, Hkv, Bq, d), q.dtype)
+    _expect(o, "o", (B, Hq, Bq, d), q.dtype)
+    _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
+    n_keep = _check_idx(idx, B, Hkv)
+    _check_gpu(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx)
+    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    st = library().blkattn_full_noalloc(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
+                                        _ref(_tensor(v_pre)), _ptr(idx), _ref(_tensor(k_blk)),
+                                        _ref(_tensor(v_blk)), _ref(_tensor(o)), _ptr(lse), _stream(stream))
     _raise(st)
     return o, lse
 

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "launch.h"
 
@@ -357,6 +358,37 @@ blkattn_tensor rows_from(const blkattn_tensor* t, int64_t row0, int eb) {
   return r;
 }
 
+// Scratch of blkattn_full_noalloc: one array per device, from the code
+// object's static data (each GPU the library runs on holds it until the
+// process ends). In host code `scratch` only names the symbol; its device
+// address on each device comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address, or nullptr (with the error) when it
+// cannot be had.
+void* device_scratch(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,6 +437,29 @@ size_t blkattn_workspace_bytes(const blkattn_dims* d, int op) {
   if (op == BLKATTN_OP_SELECT) return select_plan((int64_t)d->batch * d->kv_heads, d->prefix_len).ws_bytes;
   if (op == BLKATTN_OP_SEQUENCE) return seq_plans(d).ws;
   return ws_layout(d, s).total;
+}
+
+int blkattn_full_noalloc(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                         const blkattn_tensor* v_pre, const int32_t* idx, const blkattn_tensor* k_blk,
+                         const blkattn_tensor* v_blk, const blkattn_tensor* o, float* lse, void* stream) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (d->batch == 0 || d->q_heads == 0 || d->block_len == 0) return ok();
+  const size_t need = blkattn_workspace_bytes(d, BLKATTN_OP_FULL);
+  if (need > kNoAllocScratchBytes)
+    return fail(BLKATTN_ERR_WORKSPACE,
+                "blkattn_full_noalloc: these dims need %zu bytes of scratch, more than its %zu; "
+                "use blkattn_full with a workspace",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e;
+    ws = device_scratch(&e);
+    if (ws == nullptr)
+      return fail(BLKATTN_ERR_HIP, "blkattn_full_noalloc: no scratch address on this device: %s",
+                  hipGetErrorString(e));
+  }
+  return blkattn_full(d, q, k_pre, v_pre, idx, k_blk, v_blk, o, lse, ws, need, stream);
 }
 
 int blkattn_full(const blkattn_dims* d, const blkattn_tensor* q, const blkattn_tensor* k_pre,

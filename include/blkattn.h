@@ -148,6 +148,25 @@ int blkattn_full(const blkattn_dims* dims, const blkattn_tensor* q, const blkatt
                  size_t workspace_bytes, void* stream);
 
 /*
+ * blkattn_full_noalloc - blkattn_full for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the key-split scratch comes from an array of 64 MiB that
+ * the library holds in static device memory on every GPU it runs on, so the
+ * call allocates nothing and takes no workspace. Arguments and results are
+ * those of blkattn_full.
+ * Errors: BLKATTN_ERR_WORKSPACE when blkattn_workspace_bytes(dims,
+ * BLKATTN_OP_FULL) exceeds 64 MiB (use blkattn_full), BLKATTN_ERR_HIP when the
+ * array's address cannot be obtained on the current device.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one
+ * GPU (other streams, other threads) race and must not be issued; calls in
+ * order on one stream are safe (nothing in the array must start at zero, and
+ * each call writes every part of it that it reads).
+ */
+int blkattn_full_noalloc(const blkattn_dims* dims, const blkattn_tensor* q, const blkattn_tensor* k_pre,
+                         const blkattn_tensor* v_pre, const int32_t* idx, const blkattn_tensor* k_blk,
+                         const blkattn_tensor* v_blk, const blkattn_tensor* o, float* lse, void* stream);
+
+/*
  * blkattn_prefix_partial - partial state of the block queries over the prefix
  * only: the state FACache stores at the first denoising step of a block
  * (LaCache section 3.3.3; FlashBlock abstract, block-external attention).

@@ -779,25 +779,25 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
 // barrier that opens a slot may overwrite only ring slots whose last reader
 // ran before that barrier.
 //
-// Two waves issue the DMAs, each with its own vmcnt budget (one wave can
-// keep at most 63 loads of 1 KB in flight): wave 7, which owns no rows,
-// issues K, three tiles ahead (ring of four); wave 6 if it owns no rows, else
-// wave 3 (which shares its SIMD with wave 7 and so has time to spare), issues
-// V, three tiles ahead (ring of five: when V of tile t+3 is issued, V of
-// tile t-1 is still being read). Both issue right after a barrier and wait
-// for their tiles to land just before one, so that no computing wave waits
-// behind the memory pipeline in the middle of a phase.
+// Wave 7 owns no rows and issues every DMA, two tiles ahead, in the order
+// K0, V0, K1, V1, ...: K of tile t+2 after the barrier of slot 2t (into the
+// ring slot of K(t-1), ring of three), V of tile t+2 after that of slot 2t+1
+// (V(t-1) is still read in slot 2t+1, so the V ring has four slots). vmcnt
+// counts the wave's loads in issue order, so the wait before the barrier of
+// slot 2t leaves in flight only V(t), K(t+1) and V(t+1): K(t) and V(t-1) have
+// landed. The wave waits until at most 47 loads are counted before each group
+// of 16 so the count stays in the field's range. No computing wave waits
+// behind the memory pipeline to issue a load.
 template <int D, bool NT = false>
 __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   constexpr int NW = 8;
   constexpr int TK = 64;
-  constexpr int NSK = 4;
-  constexpr int NSV = 5;
-  constexpr int KA = NSK - 1;  // K tiles in flight ahead of the one being read
-  constexpr int VA = NSV - 2;  // V tiles issued ahead
+  constexpr int NSK = 3;
+  constexpr int NSV = 4;
+  constexpr int AHEAD = 2;  // K and V tiles issued ahead of the one being read
   constexpr int TB = TK * D * 2;
   constexpr int IPW = TB / 1024;  // DMA instructions per K (or V) tile
-  static_assert(KA * IPW < 64 && VA * IPW < 64, "vmcnt range");
+  static_assert(3 * IPW + IPW <= 64, "three tiles in flight plus one group fit the vmcnt range");
   __shared__ __attribute__((aligned(1024))) char kring[NSK * TB];
   __shared__ __attribute__((aligned(1024))) char vring[NSV * TB];
   __shared__ int32_t sidx[kIdxCap];
@@ -818,20 +818,13 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   const int T = s.nst;
   const uint32_t kring_lds = lds_addr(kring);
   const uint32_t vring_lds = lds_addr(vring);
-  const bool k_issuer = wave == NW - 1;                                   // wave-uniform
-  const bool v_issuer = wave == (p.rows_per_wg <= 32 * (NW - 2) ? NW - 2 : NW / 2 - 1);
-  auto in_range = [&](int tt) __attribute__((always_inline)) { return tt >= 0 && tt < T; };
+  const bool issuer = wave == NW - 1;  // wave-uniform; the launch leaves it without rows
   auto issue_tile = [&](bool isv, int tt) __attribute__((always_inline)) {
-    if (!in_range(tt)) return;
+    if (tt < 0 || tt >= T) return;
     const int64_t key0 = s.kbeg + (int64_t)tt * TK;
     const uint32_t dst = isv ? vring_lds + (tt % NSV) * TB : kring_lds + (tt % NSK) * TB;
+    wait_vm<63 - IPW>();
     dma_tile_all<D, TK, NT>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
-  };
-  // Tiles of [a, b] that exist, times the DMAs per tile.
-  auto insts = [&](int a, int b) __attribute__((always_inline)) {
-    const int lo = a > 0 ? a : 0;
-    const int hi = b < T - 1 ? b : T - 1;
-    return hi >= lo ? (hi - lo + 1) * IPW : 0;
   };
 
   f32x16_t sacc[TK / 32];
@@ -864,23 +857,23 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   };
 
   wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
-  if (k_issuer)
-    for (int tt = 0; tt < KA; ++tt) issue_tile(false, tt);
-  if (v_issuer)
-    for (int tt = 0; tt < VA; ++tt) issue_tile(true, tt);
+  if (issuer)
+    for (int tt = 0; tt < AHEAD; ++tt) {
+      issue_tile(false, tt);
+      issue_tile(true, tt);
+    }
   // Slot 2t opens with M(t) of the leading half, which reads K of tile t and
-  // V of tile t-1: their issuers wait until those have landed (every later
-  // DMA of theirs may still be in flight), barrier, then K of tile t+KA is
-  // issued. Slot 2t+1: barrier, then V of tile t+VA.
+  // V of tile t-1. The issuer waits until only the loads issued after K(t)
+  // remain (V(t), K(t+1), V(t+1), those that exist), barrier, then K of tile
+  // t+2 is issued. Slot 2t+1: barrier, then V of tile t+2.
   auto even_slot = [&](int t) __attribute__((always_inline)) {
-    if (k_issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(insts(t + 1, t + KA - 1));
-    if (v_issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(insts(t, t + VA - 1));
+    if (issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(IPW * ((t < T ? 1 : 0) + (t + 1 < T ? 2 : 0)));
     tile_barrier();
-    if (k_issuer) issue_tile(false, t + KA);
+    if (issuer) issue_tile(false, t + AHEAD);
   };
   auto odd_slot = [&](int t) __attribute__((always_inline)) {
     tile_barrier();
-    if (v_issuer) issue_tile(true, t + VA);
+    if (issuer) issue_tile(true, t + AHEAD);
   };
   const bool work = s.computes && T > 0;  // wave-uniform
   if (wave < NW / 2) {

@@ -14,16 +14,20 @@ here by simulation for every tile count up to 64:
 * a wave never needs more than 63 loads counted (the vmcnt field's range).
 
 The constants mirror the kernels: 64-key tiles of d = 128 bf16 (16 DMA
-instructions of 1 KB per K or V tile), K ring of 4 slots issued 3 tiles ahead
-and V ring of 5 slots issued 3 tiles ahead in the attention kernel, K ring of 4
-slots issued 3 tiles ahead by two waves (8 instructions each) in the mass
-kernel. A slot is one phase: slot 2t opens the phase that reads tile t for the
-leading half of the workgroup, slot 2t + 1 the same phase for the lagging half.
+instructions of 1 KB per K or V tile). In the attention kernel one wave (which
+owns no rows) issues both K and V, two tiles ahead each, in the order K0, V0,
+K1, V1, K2, ... (K(t + 2) after the barrier of slot 2t, V(t + 2) after that of
+slot 2t + 1), into a K ring of 3 slots and a V ring of 4, and before each
+16-instruction group it waits until at most 47 loads are counted. The mass
+kernel has a K ring of 4 slots issued 3 tiles ahead by two waves (8
+instructions each). A slot is one phase: slot 2t opens the phase that reads
+tile t for the leading half of the workgroup, slot 2t + 1 the same phase for
+the lagging half.
 """
 import pytest
 
 
-def _landed_ok(seq, need_tile, slot, allowed, ipt):
+def _landed_ok(seq, need_tile, slot, allowed, ipt):  # (mass kernel: one name per sequence)
     """seq: this wave's issues as (slot, tile), in order. At the wait before
     the barrier that opens `slot`, the issues made so far are those with an
     issue slot < `slot`; the wait leaves `allowed` instructions in flight. The
@@ -35,42 +39,65 @@ def _landed_ok(seq, need_tile, slot, allowed, ipt):
     return allowed <= after and allowed <= 63
 
 
-def _attention_schedule(T, NSK=4, NSV=5, IPT=16, KA=None, VA=None):
-    KA = NSK - 1 if KA is None else KA
-    VA = NSV - 2 if VA is None else VA
+def _attention_schedule(T, NSK=3, NSV=4, IPT=16, KA=2, VA=2):
+    """The issuing wave's single sequence of (issue slot, name, tile): the
+    prologue (slot -1) K0, V0, K1, V1, ..., then K(t + KA) after the barrier
+    of slot 2t and V(t + VA) after that of slot 2t + 1."""
     ok = lambda x: 0 <= x < T
-    # prologue issues carry slot -1; K(t + KA) after the barrier of slot 2t,
-    # V(t + VA) after the barrier of slot 2t + 1
-    K = [(-1, t) for t in range(KA) if ok(t)] + [(2 * t, t + KA) for t in range(T + 1) if ok(t + KA)]
-    V = [(-1, t) for t in range(VA) if ok(t)] + [(2 * t + 1, t + VA) for t in range(T + 1) if ok(t + VA)]
+    seq = []
+    for t in range(max(KA, VA)):
+        if t < KA and ok(t):
+            seq.append((-1, "K", t))
+        if t < VA and ok(t):
+            seq.append((-1, "V", t))
+    for t in range(T + 1):
+        if ok(t + KA):
+            seq.append((2 * t, "K", t + KA))
+        if ok(t + VA):
+            seq.append((2 * t + 1, "V", t + VA))
     # readers: K of tile t in slots 2t, 2t+1 (M(t) of each half), V of tile t
     # in slots 2t+2, 2t+3 (M(t+1), the PV part)
     reads = {"K": {t: [2 * t, 2 * t + 1] for t in range(T)},
              "V": {t: [2 * t + 2, 2 * t + 3] for t in range(T)}}
 
-    def inst(a, b):  # the kernel's count of a wave's DMA instructions for tiles [a, b]
-        lo, hi = max(a, 0), min(b, T - 1)
-        return (hi - lo + 1) * IPT if hi >= lo else 0
+    def after_k(t):  # the kernel's count of loads issued after K(t) when it waits for it
+        return IPT * ((1 if t < T else 0) + (2 if t + 1 < T else 0))
 
-    return K, V, reads, KA, VA, NSK, NSV, inst
+    return seq, reads, NSK, NSV, after_k
+
+
+def _outstanding_ok(seq, IPT, cap=47):
+    """Before each group the wave waits until at most `cap` loads are counted,
+    so that a group of IPT never takes the count past 63."""
+    return cap + IPT <= 63
+
+
+def _landed(seq, name, tile, slot, allowed, ipt):
+    done = [x for x in seq if x[0] < slot]
+    pos = [i for i, x in enumerate(done) if (x[1], x[2]) == (name, tile)]
+    assert pos, f"{name}{tile} not issued before slot {slot}"
+    after = (len(done) - 1 - pos[0]) * ipt
+    return allowed <= after and allowed <= 63
 
 
 @pytest.mark.parametrize("T", range(0, 65))
 def test_attention_pp_schedule(T):
-    K, V, reads, KA, VA, NSK, NSV, inst = _attention_schedule(T)
-    for name, seq, ns in (("K", K, NSK), ("V", V, NSV)):
-        issued = {t: q for q, t in seq}
+    seq, reads, NSK, NSV, after_k = _attention_schedule(T)
+    assert _outstanding_ok(seq, 16)
+    # issue order is one sequence: slots never go back
+    assert [x[0] for x in seq] == sorted(x[0] for x in seq)
+    for name, ns in (("K", NSK), ("V", NSV)):
+        issued = {t: q for q, n, t in seq if n == name}
         assert sorted(issued) == list(range(T)), name
-        for q, t in seq:  # ring hazard: the previous occupant's last read ended
-            if t - ns >= 0:
+        for q, n, t in seq:  # ring hazard: the previous occupant's last read ended
+            if n == name and t - ns >= 0:
                 assert max(reads[name][t - ns]) < q, (name, T, t)
         for t, slots in reads[name].items():  # issued before the barrier of its first reader
             assert issued[t] < min(slots)
-    for t in range(T + 1):  # waits before the barrier of slot 2t
-        if t < T:  # K issuer: K(t) landed, K(t+1 .. t+KA-1) may be in flight
-            assert _landed_ok(K, t, 2 * t, inst(t + 1, t + KA - 1), 16)
-        if t >= 1:  # V issuer: V(t-1) landed, V(t .. t+VA-1) may be in flight
-            assert _landed_ok(V, t - 1, 2 * t, inst(t, t + VA - 1), 16)
+    for t in range(T):  # wait before the barrier of slot 2t: K(t) and V(t-1) landed
+        assert _landed(seq, "K", t, 2 * t, after_k(t), 16)
+        if t >= 1:
+            assert _landed(seq, "V", t - 1, 2 * t, after_k(t), 16)
 
 
 @pytest.mark.parametrize("T", range(0, 65))
@@ -106,13 +133,15 @@ def test_mass_pp_schedule(T):
 
 
 def test_schedule_model_catches_mistakes():
-    # V issued three tiles ahead into a ring of four would overwrite the tile
-    # the lagging half is still reading
-    K, V, reads, KA, VA, NSK, NSV, inst = _attention_schedule(20, NSV=4, VA=3)
-    assert any(t - NSV >= 0 and max(reads["V"][t - NSV]) >= q for q, t in V)
-    # K issued four tiles ahead into a ring of four: the same for K
-    K, V, reads, KA, VA, NSK, NSV, inst = _attention_schedule(20, KA=4)
-    assert any(t - NSK >= 0 and max(reads["K"][t - NSK]) >= q for q, t in K)
-    # a wait that allows one tile more in flight than issued after K(t)
-    K, V, reads, KA, VA, NSK, NSV, inst = _attention_schedule(20)
-    assert not _landed_ok(K, 5, 10, inst(6, 5 + KA - 1) + 16, 16)
+    # a V ring of three: V(t + 2) would overwrite V(t - 1) while the lagging
+    # half still reads it
+    seq, reads, NSK, NSV, after_k = _attention_schedule(20, NSV=3)
+    assert any(n == "V" and t - NSV >= 0 and max(reads["V"][t - NSV]) >= q for q, n, t in seq)
+    # K three tiles ahead into a ring of three: the same for K
+    seq, reads, NSK, NSV, after_k = _attention_schedule(20, KA=3)
+    assert any(n == "K" and t - NSK >= 0 and max(reads["K"][t - NSK]) >= q for q, n, t in seq)
+    # a wait that allows one group more in flight than was issued after K(t)
+    seq, reads, NSK, NSV, after_k = _attention_schedule(20)
+    assert not _landed(seq, "K", 5, 10, after_k(5) + 16, 16)
+    # no cap before the groups: four groups in flight would need 64 counts
+    assert not _outstanding_ok(seq, 16, cap=48)

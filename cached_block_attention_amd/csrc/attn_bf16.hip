@@ -51,6 +51,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace blkattn {
 namespace {
 
@@ -856,58 +858,67 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
     tile_softmax<D, TK, false>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), h);
   };
 
-  wait_vm<0>();  // the query fragment and initial state have landed before any DMA is counted
-  if (issuer)
+  // Slot 2t opens with M(t) of the leading half, which reads K of tile t and
+  // V of tile t-1. The issuer waits until only the loads issued after K(t)
+  // remain (V(t), K(t+1), V(t+1), those that exist), barrier, then K of tile
+  // t+2 is issued. Slot 2t+1: barrier, then V of tile t+2. The issuing wave
+  // runs this barrier sequence in a loop of its own, so the computing waves
+  // carry no DMA code (and no registers for it).
+  using Issue = std::integral_constant<bool, true>;
+  using NoIssue = std::integral_constant<bool, false>;
+  auto even_slot = [&](int t, auto issue) __attribute__((always_inline)) {
+    if constexpr (decltype(issue)::value)
+      wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(IPW * ((t < T ? 1 : 0) + (t + 1 < T ? 2 : 0)));
+    tile_barrier();
+    if constexpr (decltype(issue)::value) issue_tile(false, t + AHEAD);
+  };
+  auto odd_slot = [&](int t, auto issue) __attribute__((always_inline)) {
+    tile_barrier();
+    if constexpr (decltype(issue)::value) issue_tile(true, t + AHEAD);
+  };
+  const bool work = s.computes && T > 0;  // wave-uniform
+  if (issuer) {
+    wait_vm<0>();  // nothing of this wave's own is counted with the DMAs
     for (int tt = 0; tt < AHEAD; ++tt) {
       issue_tile(false, tt);
       issue_tile(true, tt);
     }
-  // Slot 2t opens with M(t) of the leading half, which reads K of tile t and
-  // V of tile t-1. The issuer waits until only the loads issued after K(t)
-  // remain (V(t), K(t+1), V(t+1), those that exist), barrier, then K of tile
-  // t+2 is issued. Slot 2t+1: barrier, then V of tile t+2.
-  auto even_slot = [&](int t) __attribute__((always_inline)) {
-    if (issuer) wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(IPW * ((t < T ? 1 : 0) + (t + 1 < T ? 2 : 0)));
-    tile_barrier();
-    if (issuer) issue_tile(false, t + AHEAD);
-  };
-  auto odd_slot = [&](int t) __attribute__((always_inline)) {
-    tile_barrier();
-    if (issuer) issue_tile(true, t + AHEAD);
-  };
-  const bool work = s.computes && T > 0;  // wave-uniform
-  if (wave < NW / 2) {
+    for (int t = 0; t <= T; ++t) {
+      even_slot(t, Issue{});
+      odd_slot(t, Issue{});
+    }
+  } else if (wave < NW / 2) {
     // leading half: M(t) in slot 2t, X(t) in slot 2t+1
-    even_slot(0);
+    even_slot(0, NoIssue{});
     if (work) m_first();
-    odd_slot(0);
+    odd_slot(0, NoIssue{});
     if (work) x_phase(0);
     for (int t = 1; t < T; ++t) {
-      even_slot(t);
+      even_slot(t, NoIssue{});
       if (work) m_mid(t);
-      odd_slot(t);
+      odd_slot(t, NoIssue{});
       if (work) x_phase(t);
     }
     if (T > 0) {
-      even_slot(T);
+      even_slot(T, NoIssue{});
       if (work) m_last();
-      odd_slot(T);
+      odd_slot(T, NoIssue{});
     }
   } else {
     // lagging half: X(t-1) in slot 2t, M(t) in slot 2t+1
-    even_slot(0);
-    odd_slot(0);
+    even_slot(0, NoIssue{});
+    odd_slot(0, NoIssue{});
     if (work) m_first();
     for (int t = 1; t < T; ++t) {
-      even_slot(t);
+      even_slot(t, NoIssue{});
       if (work) x_phase(t - 1);
-      odd_slot(t);
+      odd_slot(t, NoIssue{});
       if (work) m_mid(t);
     }
     if (T > 0) {
-      even_slot(T);
+      even_slot(T, NoIssue{});
       if (work) x_phase(T - 1);
-      odd_slot(T);
+      odd_slot(T, NoIssue{});
       if (work) m_last();
     }
   }

@@ -37,9 +37,10 @@
 //    exact because l and O~ always share the same reference. The true running
 //    max is tracked separately and exported in natural-log units.
 //  * The weights enter the PV product rounded to bf16. O~ is normalised by the
-//    sum of those rounded weights (v_dot2_f32_bf16 against (1, 1)), so o is an
-//    exact convex combination of V rows with the weights actually used; l and
-//    the log-sum-exp use the sum of the unrounded weights.
+//    sum of those rounded weights, taken by the matrix core next to the PV
+//    product (one 16x16x32 MFMA per 16 keys against a selector of ones), so o
+//    is an exact convex combination of V rows with the weights actually used;
+//    l and the log-sum-exp use the sum of the unrounded weights.
 //  * Eight-wave workgroups of 129 to 224 packed rows run the two halves of
 //    the workgroup half a tile apart ("ping-pong"): waves 0-3 and 4-7 share
 //    the four SIMDs pairwise, and while one wave of a pair issues the MFMAs of
@@ -60,6 +61,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -92,6 +94,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// x of lane l ^ 32. v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second: with x in both, the first result
+// holds the other half's x in lanes 32-63 and the second in lanes 0-31.
+__device__ __forceinline__ float other_half(float x, int lane) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
@@ -309,17 +319,36 @@ __device__ __forceinline__ void tile_scores(f32x16_t (&sacc)[TK / 32], const cha
   }
 }
 
-// Adds the bf16 weights of chunk pb (8 keys of this lane) to the four partial
-// sums lh. v_dot2_f32_bf16 against (1, 1) sums two weights exactly as the PV
-// product sees them.
-__device__ __forceinline__ void sum_bf16_weights(float (&lh)[4], const bf16x8_t& pb) {
-  bf16x2_t one;
-  one[0] = (__bf16)1.0f;
-  one[1] = (__bf16)1.0f;
-  lh[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one, lh[0], false);
-  lh[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one, lh[1], false);
-  lh[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one, lh[2], false);
-  lh[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one, lh[3], false);
+// The sum of the bf16-rounded weights, taken by the matrix core: one
+// v_mfma_f32_16x16x32_bf16 per 16-key chunk, with the chunk's weights (the B
+// operand of the PV product, lane (h, n): query n) as its B operand. There
+// lane l = 32h + n stands for column n % 16 and key group 2h + n / 16, so
+// column c carries the keys of query c in the even groups and of query c + 16
+// in the odd ones. A selector A operand of zeros and ones adds the even groups
+// into rows 0-7 and the odd ones into rows 8-15, so every register of a lane
+// holds the full sum of one query: of its own query where h = n / 16 (bits 5
+// and 4 of the lane agree), else of query n ^ 16, the query of lane l ^ 16.
+// Accumulated in fp32 exactly as the PV product sees the weights; one MFMA
+// replaces four v_dot2_f32_bf16, which cannot overlap the matrix core's work.
+__device__ __forceinline__ bool lsum_lane_is_own(int lane) { return ((lane >> 5) & 1) == ((lane >> 4) & 1); }
+
+__device__ __forceinline__ bf16x8_t lsum_selector(int lane) {
+  const bool one = ((lane & 15) < 8) == (((lane >> 4) & 1) == 0);
+  bf16x8_t a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = one ? (__bf16)1.0f : (__bf16)0.0f;
+  return a;
+}
+
+__device__ __forceinline__ void sum_weights_mfma(f32x4_t& lacc, const bf16x8_t& sel, const bf16x8_t& pb) {
+  lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb, lacc, 0, 0, 0);
+}
+
+// The value of x held by the lane whose query this lane's weight sum belongs
+// to (lane l ^ 16 for the lanes that hold another query's sum).
+__device__ __forceinline__ float for_lsum_lane(float x, int lane) {
+  const float other = __shfl_xor(x, 16);
+  return lsum_lane_is_own(lane) ? x : other;
 }
 
 // Running online-softmax state of one lane's query row.
@@ -329,17 +358,18 @@ struct RowState {
   float m2;               // reference max (base 2) shared by l and O~
   float mtrue;            // exact running max (base 2)
   float lsum;             // lane-partial sum of the weights
-  float lhat;             // lane-partial sum of the bf16-rounded weights
+  f32x4_t lacc;           // sum of the bf16-rounded weights of query n or n ^ 16 (sum_weights_mfma)
 };
 
 // Eqs. 2-5 for one tile: mask keys past `nvalid`, move the reference max if
 // needed (rescaling O~ and the sums), weights P~ = 2^(s*c2 - m2) into the sum
-// l and, rounded to bf16, into the PV operand pb (chunk cc: 16 keys). With
-// LHAT the rounded weights are also summed here; otherwise the caller adds
-// them (with sum_bf16_weights) where the PV product consumes pb.
-template <int D, int TK, bool LHAT>
+// l and, rounded to bf16, into the PV operand pb (chunk cc: 16 keys). The
+// rounded weights are summed by the matrix core where the PV product
+// consumes pb (sum_weights_mfma).
+template <int D, int TK>
 __device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t (&pb)[TK / 16],
-                                             RowState<D>& st, float c2, int64_t nvalid, int h) {
+                                             RowState<D>& st, float c2, int64_t nvalid, int lane) {
+  const int h = lane >> 5;
   constexpr int NSB = TK / 32;
   if (nvalid < TK) {
     const int nv = (int)nvalid;
@@ -371,7 +401,7 @@ __device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t
     const float alpha = __builtin_amdgcn_exp2f(st.m2 - mnew);
     st.m2 = mnew;
     st.lsum *= alpha;
-    st.lhat *= alpha;
+    st.lacc *= for_lsum_lane(alpha, lane);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
   }
@@ -386,14 +416,10 @@ __device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t
       ps[r & 3] += e;
     }
   st.lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int cc = 0; cc < TK / 16; ++cc) {
+  for (int cc = 0; cc < TK / 16; ++cc)
 #pragma unroll
     for (int i = 0; i < 8; ++i) pb[cc][i] = (__bf16)sacc[cc >> 1][8 * (cc & 1) + i];
-    if (LHAT) sum_bf16_weights(lh, pb[cc]);
-  }
-  if (LHAT) st.lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
 }
 
 // O^T += V^T P^T (eq. 6) for one tile. Chunk cc covers tile keys 16*cc ..
@@ -403,8 +429,9 @@ __device__ __forceinline__ void tile_softmax(f32x16_t (&sacc)[TK / 32], bf16x8_t
 // s = lane % 16 of each 16-lane group reads V row 16*cc + 8*rr + 4*h + s/4 at
 // head-dim columns 32*db + 16*dh + 4*(s%4) .. +3.
 template <int D, int TK>
-__device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], const bf16x8_t (&pb)[TK / 16], const char* vb,
-                                        int lane) {
+__device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], f32x4_t& lacc, const bf16x8_t (&pb)[TK / 16],
+                                        const char* vb, int lane) {
+  const bf16x8_t sel = lsum_selector(lane);
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   const int h = lane >> 5;
@@ -428,6 +455,7 @@ __device__ __forceinline__ void tile_pv(f32x16_t (&oacc)[D / 32], const bf16x8_t
       }
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[db], 0, 0, 0);
+      if (db == 0) sum_weights_mfma(lacc, sel, pb[cc]);
     }
 }
 
@@ -449,7 +477,8 @@ __device__ __forceinline__ bf16x8_t lds_tr_pair(uint32_t lo, uint32_t hi) {
 template <int D, int TK>
 __device__ __forceinline__ void mfma_phase_both(f32x16_t (&oacc)[D / 32], const bf16x8_t (&pb)[TK / 16],
                                                 uint32_t va, f32x16_t (&sacc)[TK / 32], uint32_t ka,
-                                                const bf16x8_t (&qf)[D / 16], int lane, float& lhat) {
+                                                const bf16x8_t (&qf)[D / 16], int lane, f32x4_t& lacc,
+                                                const bf16x8_t& sel) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int NCC = TK / 16;
@@ -492,7 +521,6 @@ __device__ __forceinline__ void mfma_phase_both(f32x16_t (&oacc)[D / 32], const 
     }
   };
   const f32x16_t zero = {};
-  float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < PD; ++i) load(i);
 #pragma unroll
@@ -501,9 +529,7 @@ __device__ __forceinline__ void mfma_phase_both(f32x16_t (&oacc)[D / 32], const 
     if (i < NPV) {
       const int cc = i / NDB, db = i % NDB;
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[i % (PD + 1)], pb[cc], oacc[db], 0, 0, 0);
-      // the sum of the rounded weights rides in the MFMA stream: next to
-      // another wave's MFMAs the dot instruction waits for the matrix pipe
-      if (db == 0) sum_bf16_weights(lh, pb[cc]);
+      if (db == 0) sum_weights_mfma(lacc, sel, pb[cc]);
     } else {
       const int kk = (i - NPV) / NSB, sb = (i - NPV) % NSB;
       sacc[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[i % (PD + 1)], qf[kk], kk == 0 ? zero : sacc[sb],
@@ -511,7 +537,6 @@ __device__ __forceinline__ void mfma_phase_both(f32x16_t (&oacc)[D / 32], const 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
 }
 
 // Everything a workgroup needs before its tile loop.
@@ -612,7 +637,8 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const AttnParams&
 // the running (m, l, O~) of a later step starts from the cache): O~ = l * o,
 // m in base 2, l carried by the lanes of the first wave half.
 template <int D>
-__device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p, const RowInfo& s, int h) {
+__device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p, const RowInfo& s, int lane) {
+  const int h = lane >> 5;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -620,7 +646,7 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
   st.m2 = -INFINITY;
   st.mtrue = -INFINITY;
   st.lsum = 0.0f;
-  st.lhat = 0.0f;
+  float lrow = 0.0f;  // this lane's query's initial sum of the weights
   if (p.init_m != nullptr && s.row_ok) {
     const float mi = p.init_m[s.mrow];
     const float li = p.init_l[s.mrow];
@@ -628,7 +654,7 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
       st.m2 = mi * kLog2e;
       st.mtrue = st.m2;
       st.lsum = h == 0 ? li : 0.0f;
-      st.lhat = st.lsum;
+      lrow = li;
       const float* orow = p.init_o + s.mrow * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -642,14 +668,22 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
         }
     }
   }
+  const float lq = for_lsum_lane(lrow, lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st.lacc[r] = lq;
 }
 
 // Finish: o = O~ / l, L = m + ln l (natural-log units), to the final O + LSE,
 // a caller's partial, or the split workspace.
 template <int D>
-__device__ __forceinline__ void finish(const RowState<D>& st, const AttnParams& p, const RowInfo& s, int h) {
+__device__ __forceinline__ void finish(const RowState<D>& st, const AttnParams& p, const RowInfo& s, int lane) {
+  const int h = lane >> 5;
   const float ltot = pair_sum(st.lsum);
-  const float lhtot = pair_sum(st.lhat);
+  // the sum of the rounded weights of this lane's query: its own register,
+  // or that of lane l ^ 32 (which holds this query's)
+  const float lown = st.lacc[0];
+  const float lother = other_half(lown, lane);
+  const float lhtot = lsum_lane_is_own(lane) ? lown : lother;
   const bool live = ltot > 0.0f;
   const float inv = live ? 1.0f / lhtot : 0.0f;
   if (!s.row_ok) return;
@@ -730,7 +764,7 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
   {
     const RowInfo ri = row_info(p, wave, lane);
     load_q<D>(qf, p, ri, h);
-    init_state<D>(st, p, ri, h);
+    init_state<D>(st, p, ri, lane);
   }
   const uint32_t ring_lds = lds_addr(ring);
   const bool issuer = !DMAW || wave == NW;  // wave-uniform
@@ -762,10 +796,10 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
     f32x16_t sacc[TK / 32];
     bf16x8_t pb[TK / 16];
     tile_scores<D, TK>(sacc, kb, qf, n, h);
-    tile_softmax<D, TK, true>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), h);
-    tile_pv<D, TK>(st.oacc, pb, kb + TB, lane);
+    tile_softmax<D, TK>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), lane);
+    tile_pv<D, TK>(st.oacc, st.lacc, pb, kb + TB, lane);
   }
-  finish<D>(st, p, row_info(p, wave, opaque(lane)), h);
+  finish<D>(st, p, row_info(p, wave, opaque(lane)), lane);
 }
 
 // Eight waves (at most 224 packed rows), ping-pong. Per tile t every wave runs
@@ -814,12 +848,13 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   {
     const RowInfo ri = row_info(p, wave, lane);
     load_q<D>(qf, p, ri, h);
-    init_state<D>(st, p, ri, h);
+    init_state<D>(st, p, ri, lane);
   }
 
   const int T = s.nst;
   const uint32_t kring_lds = lds_addr(kring);
   const uint32_t vring_lds = lds_addr(vring);
+  const bf16x8_t lsel = lsum_selector(lane);
   const bool issuer = wave == NW - 1;  // wave-uniform; the launch leaves it without rows
   auto issue_tile = [&](bool isv, int tt) __attribute__((always_inline)) {
     if (tt < 0 || tt >= T) return;
@@ -842,20 +877,16 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   auto m_mid = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     mfma_phase_both<D, TK>(st.oacc, pb, vring_lds + ((t - 1) % NSV) * TB, sacc, kring_lds + (t % NSK) * TB, qf,
-                           lane, st.lhat);
+                           lane, st.lacc, lsel);
     __builtin_amdgcn_s_setprio(0);
   };
   auto m_last = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    tile_pv<D, TK>(st.oacc, pb, vring + ((T - 1) % NSV) * TB, lane);
-    float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int cc = 0; cc < TK / 16; ++cc) sum_bf16_weights(lh, pb[cc]);
-    st.lhat += (lh[0] + lh[1]) + (lh[2] + lh[3]);
+    tile_pv<D, TK>(st.oacc, st.lacc, pb, vring + ((T - 1) % NSV) * TB, lane);
     __builtin_amdgcn_s_setprio(0);
   };
   auto x_phase = [&](int t) __attribute__((always_inline)) {
-    tile_softmax<D, TK, false>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), h);
+    tile_softmax<D, TK>(sacc, pb, st, p.scale_log2, s.kr.n_all - (s.kbeg + (int64_t)t * TK), lane);
   };
 
   // Slot 2t opens with M(t) of the leading half, which reads K of tile t and
@@ -922,7 +953,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
       if (work) m_last();
     }
   }
-  finish<D>(st, p, row_info(p, wave, opaque(lane)), h);
+  finish<D>(st, p, row_info(p, wave, opaque(lane)), lane);
 }
 
 // Launch shapes: NW waves per workgroup (each 32 packed rows), TK keys per

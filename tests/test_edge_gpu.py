@@ -89,6 +89,21 @@ def hdr_inputs(sh, q_scale: float):
     return inp
 
 
+def row_scaled_inputs(sh):
+    """Random queries whose scale depends on the row's place in its 32-row
+    block (0.25 * 2^(r % 32 / 4), up to about 54): every row of a block has its
+    own dynamic range, so the per-row sums of the weights all differ, and a
+    sum that reached the wrong row of its block would show."""
+    inp = datagen.make_inputs(sh)
+    B, Hq, Bq, d = inp.q.shape
+    q = datagen.bf16_bits_to_f32(inp.q)
+    G = sh.q_heads // sh.kv_heads
+    packed = (np.arange(Hq) % G)[:, None] * Bq + np.arange(Bq)[None, :]  # packed row of (q-head, query)
+    scale = (0.25 * 2.0 ** ((packed % 32) / 4.0)).astype(np.float32)
+    inp.q = bf(q * scale[None, :, :, None])
+    return inp
+
+
 def run_and_compare(ba, sh, inp, splits):
     import torch
     t = {k: up(getattr(inp, k)) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
@@ -141,6 +156,14 @@ def test_high_dynamic_range_scores(ba, kw, q_scale):
     sh = datagen.scaled_shape("dream_gqa", **kw)
     say(f"case hdr q x{q_scale} {sh}")
     run_and_compare(ba, sh, hdr_inputs(sh, q_scale), 3)
+
+
+@pytest.mark.parametrize("kw", SHAPES, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+@pytest.mark.parametrize("splits", [0, 3])
+def test_row_dependent_score_scale(ba, kw, splits):
+    sh = datagen.scaled_shape("dream_gqa", **kw)
+    say(f"case row-scaled q {sh} splits={splits}")
+    run_and_compare(ba, sh, row_scaled_inputs(sh), splits)
 
 
 def test_one_hot_full_size_metric_workload_sampled(ba):

@@ -197,6 +197,43 @@ __device__ __forceinline__ void dma_tile_contig(const char* sbase, bool isv, uin
   }
 }
 
+// The per-lane offsets of dma_tile_contig for every DMA of a K and a V tile,
+// for a wave that issues many tiles and has registers to spare: computed
+// once, they make each later contiguous tile a run of scalar-addressed DMAs
+// with no vector work.
+template <int D, int TK>
+struct ContigLanes {
+  static constexpr int INT = TK * D * 2 / 1024;
+  uint32_t k[INT];
+  uint32_t v[INT];
+};
+
+template <int D, int TK>
+__device__ __forceinline__ ContigLanes<D, TK> contig_lanes(int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int RPI = 1024 / ROWB;
+  ContigLanes<D, TK> c;
+  const int rl = lane / CPR;
+  const int cl = lane % CPR;
+#pragma unroll
+  for (int j = 0; j < ContigLanes<D, TK>::INT; ++j) {
+    const int r = j * RPI + rl;
+    c.k[j] = (uint32_t)(rl * ROWB + 16 * (cl ^ swz_k<CPR>(r)));
+    c.v[j] = (uint32_t)(rl * ROWB + 16 * (cl ^ swz_v<CPR>(r)));
+  }
+  return c;
+}
+
+template <int D, int TK, bool NT = false>
+__device__ __forceinline__ void dma_tile_contig_pre(const char* sbase, const uint32_t (&off)[TK * D * 2 / 1024],
+                                                    uint32_t dst) {
+  constexpr int INT = TK * D * 2 / 1024;
+#pragma unroll
+  for (int g = 0; g < INT / 4; ++g)
+    dma_4k_s<NT>(sbase + 4096 * g, off[4 * g], off[4 * g + 1], off[4 * g + 2], off[4 * g + 3], dst + 4096 * g);
+}
+
 // A tile of retained (gathered) prefix rows whose byte offsets from the head's
 // first row fit 31 bits: scalar head base plus per-lane offsets from the
 // staged indices.
@@ -285,6 +322,20 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
   }
 #pragma unroll 1
   for (int k = 0; k < INT; ++k) dma_one<D, TK>(kr, isv, key0, dst, k, lane, sidx, kbeg);
+}
+
+// dma_tile_all for a wave holding the contiguous path's lane offsets.
+template <int D, int TK, bool NT = false>
+__device__ __forceinline__ void dma_tile_all_pre(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int lane,
+                                                 const int32_t* sidx, int64_t kbeg, const ContigLanes<D, TK>& cl) {
+  if (tile_is_fast<TK>(kr, key0)) {
+    const SegTile f = seg_tile<TK>(kr, isv, key0);
+    if (f.valid == TK && f.st == 2 * D) {
+      dma_tile_contig_pre<D, TK, NT>(f.base, isv ? cl.v : cl.k, dst);
+      return;
+    }
+  }
+  dma_tile_all<D, TK, NT>(kr, isv, key0, dst, lane, sidx, kbeg);
 }
 
 // This wave's share of the DMA of one K (or V) tile: with NW waves issuing,
@@ -856,12 +907,13 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   const uint32_t vring_lds = lds_addr(vring);
   const bf16x8_t lsel = lsum_selector(lane);
   const bool issuer = wave == NW - 1;  // wave-uniform; the launch leaves it without rows
-  auto issue_tile = [&](bool isv, int tt) __attribute__((always_inline)) {
+  // (issuer only) cl: the contiguous path's lane offsets, computed once
+  auto issue_tile = [&](bool isv, int tt, const ContigLanes<D, TK>& cl) __attribute__((always_inline)) {
     if (tt < 0 || tt >= T) return;
     const int64_t key0 = s.kbeg + (int64_t)tt * TK;
     const uint32_t dst = isv ? vring_lds + (tt % NSV) * TB : kring_lds + (tt % NSK) * TB;
     wait_vm<63 - IPW>();
-    dma_tile_all<D, TK, NT>(s.kr, isv, key0, dst, lane, sidx, s.kbeg);
+    dma_tile_all_pre<D, TK, NT>(s.kr, isv, key0, dst, lane, sidx, s.kbeg, cl);
   };
 
   f32x16_t sacc[TK / 32];
@@ -897,59 +949,61 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   // carry no DMA code (and no registers for it).
   using Issue = std::integral_constant<bool, true>;
   using NoIssue = std::integral_constant<bool, false>;
-  auto even_slot = [&](int t, auto issue) __attribute__((always_inline)) {
+  auto even_slot = [&](int t, auto issue, const auto& cl) __attribute__((always_inline)) {
     if constexpr (decltype(issue)::value)
       wait_at_most<3 * IPW, 2 * IPW, IPW, 0>(IPW * ((t < T ? 1 : 0) + (t + 1 < T ? 2 : 0)));
     tile_barrier();
-    if constexpr (decltype(issue)::value) issue_tile(false, t + AHEAD);
+    if constexpr (decltype(issue)::value) issue_tile(false, t + AHEAD, cl);
   };
-  auto odd_slot = [&](int t, auto issue) __attribute__((always_inline)) {
+  auto odd_slot = [&](int t, auto issue, const auto& cl) __attribute__((always_inline)) {
     tile_barrier();
-    if constexpr (decltype(issue)::value) issue_tile(true, t + AHEAD);
+    if constexpr (decltype(issue)::value) issue_tile(true, t + AHEAD, cl);
   };
   const bool work = s.computes && T > 0;  // wave-uniform
+  const int none = 0;                      // the computing waves pass no lane offsets
   if (issuer) {
+    const ContigLanes<D, TK> cl = contig_lanes<D, TK>(lane);
     wait_vm<0>();  // nothing of this wave's own is counted with the DMAs
     for (int tt = 0; tt < AHEAD; ++tt) {
-      issue_tile(false, tt);
-      issue_tile(true, tt);
+      issue_tile(false, tt, cl);
+      issue_tile(true, tt, cl);
     }
     for (int t = 0; t <= T; ++t) {
-      even_slot(t, Issue{});
-      odd_slot(t, Issue{});
+      even_slot(t, Issue{}, cl);
+      odd_slot(t, Issue{}, cl);
     }
   } else if (wave < NW / 2) {
     // leading half: M(t) in slot 2t, X(t) in slot 2t+1
-    even_slot(0, NoIssue{});
+    even_slot(0, NoIssue{}, none);
     if (work) m_first();
-    odd_slot(0, NoIssue{});
+    odd_slot(0, NoIssue{}, none);
     if (work) x_phase(0);
     for (int t = 1; t < T; ++t) {
-      even_slot(t, NoIssue{});
+      even_slot(t, NoIssue{}, none);
       if (work) m_mid(t);
-      odd_slot(t, NoIssue{});
+      odd_slot(t, NoIssue{}, none);
       if (work) x_phase(t);
     }
     if (T > 0) {
-      even_slot(T, NoIssue{});
+      even_slot(T, NoIssue{}, none);
       if (work) m_last();
-      odd_slot(T, NoIssue{});
+      odd_slot(T, NoIssue{}, none);
     }
   } else {
     // lagging half: X(t-1) in slot 2t, M(t) in slot 2t+1
-    even_slot(0, NoIssue{});
-    odd_slot(0, NoIssue{});
+    even_slot(0, NoIssue{}, none);
+    odd_slot(0, NoIssue{}, none);
     if (work) m_first();
     for (int t = 1; t < T; ++t) {
-      even_slot(t, NoIssue{});
+      even_slot(t, NoIssue{}, none);
       if (work) x_phase(t - 1);
-      odd_slot(t, NoIssue{});
+      odd_slot(t, NoIssue{}, none);
       if (work) m_mid(t);
     }
     if (T > 0) {
-      even_slot(T, NoIssue{});
+      even_slot(T, NoIssue{}, none);
       if (work) x_phase(T - 1);
-      odd_slot(T, NoIssue{});
+      odd_slot(T, NoIssue{}, none);
       if (work) m_last();
     }
   }

@@ -230,7 +230,7 @@ def config_lines(reps: int, with_cpu: bool, which):
         emit({"config": "C1 tiny_f32: f32 B1 H4/4 d64 P256 Bq32", "function": "blkattn_full",
               "kernel_ms": s["ms"], "kernel_ms_p10": s["ms_p10"], "kernel_ms_p90": s["ms_p90"],
               "tflops": round(alg["flops"] / (s["ms"] * 1e-3) / 1e12, 4),
-              "note": "launch-latency bound (0.66 MB, 9.4 MFLOP); the target is parity only",
+              "note": "latency bound: 0.66 MB and 9.4 MFLOP over 36 workgroups of one 32-key tile each, inputs cold after the flush; the target is parity only",
               "roofline": roofline("hbm", alg["kernel_bytes"], s["ms"], "attn_f32_kernel",
                                    {"algorithmic_bytes_per_launch": alg["kernel_bytes"], "flushed": True}),
               "cpu_baseline": cpu})

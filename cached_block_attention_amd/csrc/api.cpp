@@ -136,9 +136,16 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
   const int64_t G = d->q_heads / d->kv_heads;
   const int64_t R = G * d->block_len;
   if (d->dtype == BLKATTN_F32) {
+    // One workgroup per (split, q-head, batch) walks its 32-key tiles one
+    // after another, each tile a latency-bound chain: spread the tiles over
+    // the compute units, down to one tile per split.
     pl.tile_keys = 32;
     pl.tiles = (int)((n_keys + pl.tile_keys - 1) / pl.tile_keys);
-    pl.splits = (int)plan_splits(d, pl, (int64_t)d->batch * d->q_heads, 8, n_keys, indexed);
+    const int64_t base = (int64_t)d->batch * d->q_heads;
+    int64_t sp = d->splits > 0 ? d->splits : (kComputeUnits + base - 1) / base;
+    if (sp > pl.tiles) sp = pl.tiles;
+    if (sp < 1) sp = 1;
+    pl.splits = (int)sp;
     return pl;
   }
   // Packed-row chunks of at most `cap` rows, one workgroup each per key split.

@@ -88,14 +88,25 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
         *(float4*)&vs[key][4 * c] = vv;
       }
       __syncthreads();
+      // scores: the head dimension outermost, so that the tile's keys are 32
+      // independent FMA chains
       float s[kF32Tile];
+#pragma unroll
+      for (int j = 0; j < kF32Tile; ++j) s[j] = 0.0f;
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4)
+#pragma unroll
+        for (int j = 0; j < kF32Tile; ++j) {
+          const float4 k4 = *(const float4*)&ks[j][4 * d4];
+          s[j] = fmaf(q[4 * d4 + 0], k4.x, s[j]);
+          s[j] = fmaf(q[4 * d4 + 1], k4.y, s[j]);
+          s[j] = fmaf(q[4 * d4 + 2], k4.z, s[j]);
+          s[j] = fmaf(q[4 * d4 + 3], k4.w, s[j]);
+        }
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < kF32Tile; ++j) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int d = 0; d < D; ++d) acc = fmaf(q[d], ks[j][d], acc);
-        s[j] = j < nvalid ? acc * scale : -INFINITY;
+        s[j] = j < nvalid ? s[j] * scale : -INFINITY;
         mx = fmaxf(mx, s[j]);
       }
       const float mnew = fmaxf(m, mx);

@@ -113,8 +113,12 @@ def test_split_plan_is_a_function_of_dims(lib):
     d1 = dims(splits=1)
     assert lib.blkattn_plan_splits(ctypes.byref(d1), ba.OP_FULL) == 1
     assert lib.blkattn_workspace_bytes(ctypes.byref(d1), ba.OP_FULL) == 0
+    # fp32: 4 (batch, q-head) workgroups per split, so its 32-key tiles are
+    # spread one per split at this size ((256 + 32) / 32 = 9)
     tiny = dims(batch=1, q_heads=4, kv_heads=4, head_dim=64, prefix_len=256, dtype=ba.F32)
-    assert lib.blkattn_plan_splits(ctypes.byref(tiny), ba.OP_FULL) == 1
+    assert lib.blkattn_plan_splits(ctypes.byref(tiny), ba.OP_FULL) == 9
+    tiny1 = dims(batch=1, q_heads=4, kv_heads=4, head_dim=64, prefix_len=256, dtype=ba.F32, splits=2)
+    assert lib.blkattn_plan_splits(ctypes.byref(tiny1), ba.OP_FULL) == 2
     huge = dims(splits=100000)
     assert lib.blkattn_plan_splits(ctypes.byref(huge), ba.OP_FULL) == (32768 + 32 + 63) // 64
     # an indexed prefix stages at most 2048 indices per split

@@ -19,6 +19,53 @@
 namespace blkattn {
 namespace {
 
+// Row `row` of the packed (b, hq, qi) order at its place in the per-row
+// arrays of the outputs (and of explicit sources): the row map may leave a
+// hole of q_hole_len rows at q_hole and pitch the heads by row_pitch.
+__device__ __forceinline__ int64_t mapped_row(const MergeParams& p, int64_t row) {
+  const int64_t hb = row / p.block_len;  // b * Hq + hq
+  const int64_t qi = row - hb * p.block_len;
+  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);  // sequence row
+  return hb * p.rows.row_pitch + srow;
+}
+
+// o = acc / L, LSE = M + ln L (or the empty state) for the 4 head-dim values
+// c4 of packed row `row`, to the final O (+ LSE) and/or the merged partial.
+template <int D>
+__device__ __forceinline__ void store_merged(const MergeParams& p, int64_t row, int c4, float M, float L,
+                                             float4 acc) {
+  const int64_t hb = row / p.block_len;
+  const int64_t qi = row - hb * p.block_len;
+  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);
+  const int64_t mrow = hb * p.rows.row_pitch + srow;
+  const bool live = L > 0.0f;
+  const float inv = live ? 1.0f / L : 0.0f;
+  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const float mo = live ? M : -INFINITY;
+
+  if (p.o_final != nullptr) {
+    const int64_t b = hb / p.q_heads, hq = hb - (hb / p.q_heads) * p.q_heads;
+    const int64_t off = b * p.o_sb + hq * p.o_sh + srow * p.o_st + 4 * c4;
+    if (p.out_dtype == 0) {
+      *(float4*)((float*)p.o_final + off) = o;
+    } else {
+      const __bf16 v0 = (__bf16)o.x, v1 = (__bf16)o.y, v2 = (__bf16)o.z, v3 = (__bf16)o.w;
+      uint2 w;
+      w.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+      w.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+      *(uint2*)((uint16_t*)p.o_final + off) = w;
+    }
+  }
+  if (p.lse != nullptr && c4 == 0) p.lse[mrow] = live ? M + logf(L) : -INFINITY;
+  if (p.out_o != nullptr) {
+    *(float4*)(p.out_o + mrow * D + 4 * c4) = o;
+    if (c4 == 0) {
+      p.out_m[mrow] = mo;
+      p.out_l[mrow] = live ? L : 0.0f;
+    }
+  }
+}
+
 // One thread merges 4 consecutive head-dim values of one row; D/4 threads of
 // the same wave share a row, so a row's m and l are read by all of its lanes in
 // the same instruction, before any lane writes them (safe in-place update).
@@ -33,10 +80,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
-  const int64_t hb = row / p.block_len;  // b * Hq + hq
-  const int64_t qi = row - hb * p.block_len;
-  const int64_t srow = qi + (qi >= p.rows.q_hole ? p.rows.q_hole_len : 0);  // sequence row
-  const int64_t mrow = hb * p.rows.row_pitch + srow;                      // per-row arrays
+  const int64_t mrow = mapped_row(p, row);  // explicit sources are at mapped rows
 
   float M = -INFINITY;
   float L = 0.0f;
@@ -86,32 +130,71 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     }
     M = mc;
   }
-  const bool live = L > 0.0f;
-  const float inv = live ? 1.0f / L : 0.0f;
-  const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  const float mo = live ? M : -INFINITY;
+  store_merged<D>(p, row, c4, M, L, acc);
+}
 
-  if (p.o_final != nullptr) {
-    const int64_t b = hb / p.q_heads, hq = hb - (hb / p.q_heads) * p.q_heads;
-    const int64_t off = b * p.o_sb + hq * p.o_sh + srow * p.o_st + 4 * c4;
-    if (p.out_dtype == 0) {
-      *(float4*)((float*)p.o_final + off) = o;
-    } else {
-      const __bf16 v0 = (__bf16)o.x, v1 = (__bf16)o.y, v2 = (__bf16)o.z, v3 = (__bf16)o.w;
-      uint2 w;
-      w.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-      w.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-      *(uint2*)((uint16_t*)p.o_final + off) = w;
+// The same merge over the split workspace of one attention call: nsrc
+// partials of split_rows packed rows, split s at row s * split_rows of every
+// array. A thread's loads share one 32-bit lane offset from a wave-uniform
+// base per split (the host checks that a split's o array spans less than
+// 2 GiB), and the weights are base-2 exponentials of prescaled differences,
+// one v_exp_f32 each, so a split costs a thread about a dozen instructions.
+template <int D, int CH>
+__global__ __launch_bounds__(256) void merge_split_kernel(const MergeParams p) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  constexpr float kLog2eF = 1.4426950408889634f;
+  const int64_t rows = p.split_rows;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const uint32_t ooff = (uint32_t)row * (uint32_t)(4 * D) + 16u * (uint32_t)c4;
+  const uint32_t roff = 4u * (uint32_t)row;
+  const uint64_t ostride = (uint64_t)p.split_rows * (4 * D);  // bytes from one split to the next
+  const uint64_t rstride = (uint64_t)p.split_rows * 4;
+  const char* obase = (const char*)p.src_o[0];
+  const char* mbase = (const char*)p.src_m[0];
+  const char* lbase = (const char*)p.src_l[0];
+
+  float M = -INFINITY;
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < p.nsrc; s0 += CH) {
+    float ms[CH], ls[CH];
+    float4 os[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      // past the last split: load the last one again (no branch), weight 0 below
+      const int s = s0 + i < p.nsrc ? s0 + i : p.nsrc - 1;
+      ms[i] = *(const float*)(mbase + (uint64_t)s * rstride + roff);
+      ls[i] = *(const float*)(lbase + (uint64_t)s * rstride + roff);
+      os[i] = *(const float4*)(obase + (uint64_t)s * ostride + ooff);
     }
-  }
-  if (p.lse != nullptr && c4 == 0) p.lse[mrow] = live ? M + logf(L) : -INFINITY;
-  if (p.out_o != nullptr) {
-    *(float4*)(p.out_o + mrow * D + 4 * c4) = o;
-    if (c4 == 0) {
-      p.out_m[mrow] = mo;
-      p.out_l[mrow] = live ? L : 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (s0 + i >= p.nsrc) ms[i] = -INFINITY;
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) mc = fmaxf(mc, ms[i]);
+    if (mc == -INFINITY) continue;  // every partial so far is empty
+    const float mc2 = mc * kLog2eF;
+    if (M != -INFINITY) {
+      const float sc = __builtin_amdgcn_exp2f(fmaf(M, kLog2eF, -mc2));
+      L *= sc;
+      acc.x *= sc, acc.y *= sc, acc.z *= sc, acc.w *= sc;
     }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float w = (ms[i] == -INFINITY) ? 0.0f : ls[i] * __builtin_amdgcn_exp2f(fmaf(ms[i], kLog2eF, -mc2));
+      L += w;
+      acc.x = fmaf(w, os[i].x, acc.x);
+      acc.y = fmaf(w, os[i].y, acc.y);
+      acc.z = fmaf(w, os[i].z, acc.z);
+      acc.w = fmaf(w, os[i].w, acc.w);
+    }
+    M = mc;
   }
+  store_merged<D>(p, row, c4, M, L, acc);
 }
 
 // One thread copies one 16-byte chunk of one retained row of K and of V.
@@ -154,12 +237,21 @@ __global__ __launch_bounds__(256) void fill_empty_kernel(float* o, float* m, flo
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.q_heads * p.block_len;
   if (rows == 0) return hipSuccess;
+  // the split workspace, when a lane offset into one split's o array fits 31 bits
+  const bool split_ws = p.strided != 0 && p.split_rows == rows &&
+                        (int64_t)p.split_rows * p.head_dim * 4 <= ((int64_t)1 << 31);
   if (p.head_dim == 128) {
     const int64_t blocks = (rows + 7) / 8;
-    hipLaunchKernelGGL((merge_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (split_ws)
+      hipLaunchKernelGGL((merge_split_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else if (p.head_dim == 64) {
     const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL((merge_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (split_ws)
+      hipLaunchKernelGGL((merge_split_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

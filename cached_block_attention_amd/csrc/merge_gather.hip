@@ -66,12 +66,13 @@ __device__ __forceinline__ void store_merged(const MergeParams& p, int64_t row, 
   }
 }
 
-// One thread merges 4 consecutive head-dim values of one row; D/4 threads of
-// the same wave share a row, so a row's m and l are read by all of its lanes in
+// Two explicit partials (blkattn_merge), at the rows of the row map. One
+// thread merges 4 consecutive head-dim values of one row; D/4 threads of the
+// same wave share a row, so a row's m and l are read by all of its lanes in
 // the same instruction, before any lane writes them (safe in-place update).
 // The partials are consumed in chunks of CH: all loads of a chunk are issued
 // before any is used, then folded into a running (M, L, acc) with the merge
-// formula, in fixed split order.
+// formula, in fixed order.
 template <int D, int CH>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   constexpr int TPR = D / 4;
@@ -95,19 +96,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
       ls[i] = 0.0f;
       os[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (s < p.nsrc) {
-        const float* po;
-        if (p.strided) {
-          const int64_t e = (int64_t)s * p.split_rows + row;
-          ms[i] = p.src_m[0][e];
-          ls[i] = p.src_l[0][e];
-          po = p.src_o[0] + e * D;
-        } else {
-          const int si = s < 2 ? s : 1;  // two explicit sources
-          ms[i] = p.src_m[si][mrow];
-          ls[i] = p.src_l[si][mrow];
-          po = p.src_o[si] + mrow * D;
-        }
-        os[i] = *(const float4*)(po + 4 * c4);
+        const int si = s < 2 ? s : 1;  // two explicit sources
+        ms[i] = p.src_m[si][mrow];
+        ls[i] = p.src_l[si][mrow];
+        os[i] = *(const float4*)(p.src_o[si] + mrow * D + 4 * c4);
       }
     }
     float mc = M;
@@ -135,9 +127,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 // The same merge over the split workspace of one attention call: nsrc
 // partials of split_rows packed rows, split s at row s * split_rows of every
-// array. A thread's loads share one 32-bit lane offset from a wave-uniform
-// base per split (the host checks that a split's o array spans less than
-// 2 GiB), and the weights are base-2 exponentials of prescaled differences,
+// array. A thread's loads share one lane offset from a wave-uniform base per
+// split, and the weights are base-2 exponentials of prescaled differences,
 // one v_exp_f32 each, so a split costs a thread about a dozen instructions.
 template <int D, int CH>
 __global__ __launch_bounds__(256) void merge_split_kernel(const MergeParams p) {
@@ -148,8 +139,8 @@ __global__ __launch_bounds__(256) void merge_split_kernel(const MergeParams p) {
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
-  const uint32_t ooff = (uint32_t)row * (uint32_t)(4 * D) + 16u * (uint32_t)c4;
-  const uint32_t roff = 4u * (uint32_t)row;
+  const uint64_t ooff = (uint64_t)row * (4 * D) + 16u * (uint32_t)c4;
+  const uint64_t roff = 4u * (uint64_t)row;
   const uint64_t ostride = (uint64_t)p.split_rows * (4 * D);  // bytes from one split to the next
   const uint64_t rstride = (uint64_t)p.split_rows * 4;
   const char* obase = (const char*)p.src_o[0];
@@ -237,21 +228,21 @@ __global__ __launch_bounds__(256) void fill_empty_kernel(float* o, float* m, flo
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.q_heads * p.block_len;
   if (rows == 0) return hipSuccess;
-  // the split workspace, when a lane offset into one split's o array fits 31 bits
-  const bool split_ws = p.strided != 0 && p.split_rows == rows &&
-                        (int64_t)p.split_rows * p.head_dim * 4 <= ((int64_t)1 << 31);
+  // the split workspace of one call (packed rows), else two explicit sources
+  if (p.strided != 0 && p.split_rows != rows) return hipErrorInvalidValue;
+  const bool split_ws = p.strided != 0;
   if (p.head_dim == 128) {
     const int64_t blocks = (rows + 7) / 8;
     if (split_ws)
       hipLaunchKernelGGL((merge_split_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((merge_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((merge_kernel<128, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else if (p.head_dim == 64) {
     const int64_t blocks = (rows + 15) / 16;
     if (split_ws)
       hipLaunchKernelGGL((merge_split_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((merge_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((merge_kernel<64, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

@@ -135,6 +135,16 @@ def test_one_hot_maximum_arrives_late(ba, kw, where, splits):
     run_and_compare(ba, sh, one_hot_inputs(sh, where), splits)
 
 
+@pytest.mark.parametrize("kw", [SHAPES[1], dict(batch=1, q_heads=4, kv_heads=4, prefix_len=2500, block_len=32)],
+                         ids=["pingpong", "mha"])
+def test_one_hot_maximum_in_a_late_merge_chunk(ba, kw):
+    # the winning key in the last of 20 splits: in the second chunk of 16
+    # partials that the split merge folds
+    sh = datagen.scaled_shape("dream_gqa", outlier_frac=0.0, **kw)
+    say(f"case one-hot last_prefix {sh} splits=20")
+    run_and_compare(ba, sh, one_hot_inputs(sh, "last_prefix"), 20)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_one_hot_maximum_in_a_retained_row(ba, splits):
     sh = datagen.scaled_shape("sparse_gqa", prefix_len=6000, n_keep=1500)

@@ -96,6 +96,36 @@ def test_full_with_outliers(ba):
     check_full(ba, sh)
 
 
+# More partials than one chunk of the split merge, which folds them 16 at a
+# time and carries the running max and sum from chunk to chunk (the last chunk
+# ragged): forced split counts past 16 for each kernel family, for the final
+# output and for a caller's partial.
+@pytest.mark.parametrize("name,kw,splits", [
+    ("dream_gqa", dict(batch=1, prefix_len=8192), 17),
+    ("dream_gqa", dict(batch=1, prefix_len=8192), 40),
+    ("llada_bf16", dict(q_heads=4, kv_heads=4, prefix_len=4096), 33),
+    ("tiny_f32", dict(prefix_len=2048), 19),
+])
+def test_full_many_splits(ba, name, kw, splits):
+    import torch
+    sh = shape(name, **kw)
+    q = torch.empty(sh.batch, sh.q_heads, sh.block_len, sh.head_dim, device="cuda",
+                    dtype=torch.float32 if sh.dtype == datagen.F32 else torch.bfloat16)
+    assert ba.plan_splits(ba.make_dims(q, sh.kv_heads, sh.prefix_len, splits=splits), ba.OP_FULL) == splits
+    check_full(ba, sh, splits=splits)
+
+
+def test_prefix_partial_many_splits(ba):
+    import torch
+    sh = shape(batch=1, prefix_len=8192)
+    say(f"case prefix partial {sh} splits=24")
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"], splits=24)
+    torch.cuda.synchronize()
+    _check_partial(pp, _partial_ref(inp, sh, True), sh.dtype)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 4])
 def test_full_gathered_prefix(ba, splits):
     check_full(ba, datagen.scaled_shape("sparse_gqa", prefix_len=3000, n_keep=700), splits=splits)

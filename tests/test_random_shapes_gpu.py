@@ -55,7 +55,7 @@ def test_cases_cover_every_kernel_path():
     assert any(r <= 32 for r in rows)
     assert any(32 < r <= 128 for r in rows)
     assert any(128 < r <= 192 for r in rows)     # ping-pong with an idle row wave
-    assert any(192 < r <= 224 for r in rows)     # ping-pong, V issued by wave 3
+    assert any(192 < r <= 224 for r in rows)     # ping-pong, all seven row waves
     assert any(224 < r <= 256 for r in rows)     # eight-wave sequential
     assert any(r > 256 for r in rows)            # several row chunks
     assert any(c[0]["dtype"] == datagen.F32 for c in CASES)

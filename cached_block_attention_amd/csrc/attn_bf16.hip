@@ -242,19 +242,30 @@ __device__ __forceinline__ bool tile_is_gather(const KeyRows& kr, int64_t key0) 
   return kr.indexed && kr.gather32 && key0 + TK <= kr.n_pre;
 }
 
+// The DMA of one gathered tile: every instruction's staged index is read
+// before the first DMA goes out. The DMA asm may touch memory, so an index
+// read placed between two of them waits out a full LDS round trip before its
+// own DMA; read first, the tile pays that latency once.
 template <int D, int TK>
-__device__ __forceinline__ void dma_one_gather(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int k,
-                                               int lane, const int32_t* sidx, int64_t kbeg) {
+__device__ __forceinline__ void dma_tile_gather(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int lane,
+                                                const int32_t* sidx, int64_t kbeg) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int RPI = 1024 / ROWB;
+  constexpr int INT = TK * ROWB / 1024;
   const char* sbase = uniform_ptr(isv ? kr.vpre : kr.kpre);
   const uint32_t st = (uint32_t)(isv ? kr.vp_st : kr.kp_st);
   const int ln = opaque(lane);
-  const int r = k * RPI + ln / CPR;
-  const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
-  const uint32_t row = (uint32_t)sidx[key0 - kbeg + r];
-  dma_1k_s(sbase, row * st + 16 * lc, dst + k * 1024);
+  const int32_t* tidx = sidx + (key0 - kbeg);
+  uint32_t row[INT];
+#pragma unroll
+  for (int k = 0; k < INT; ++k) row[k] = (uint32_t)tidx[k * RPI + ln / CPR];
+#pragma unroll
+  for (int k = 0; k < INT; ++k) {
+    const int r = k * RPI + ln / CPR;
+    const int lc = (ln % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+    dma_1k_s(sbase, row[k] * st + 16 * lc, dst + k * 1024);
+  }
 }
 
 // DMA instruction k of the K (isv = false) or V rows of one TK-key tile
@@ -316,8 +327,7 @@ __device__ __forceinline__ void dma_tile_all(const KeyRows& kr, bool isv, int64_
     return;
   }
   if (tile_is_gather<TK>(kr, key0)) {
-#pragma unroll
-    for (int k = 0; k < INT; ++k) dma_one_gather<D, TK>(kr, isv, key0, dst, k, lane, sidx, kbeg);
+    dma_tile_gather<D, TK>(kr, isv, key0, dst, lane, sidx, kbeg);
     return;
   }
 #pragma unroll 1

@@ -354,6 +354,27 @@ template <int D, int TK, int NW>
 __device__ __forceinline__ void dma_tile(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int wave,
                                          int lane, const int32_t* sidx, int64_t kbeg) {
   constexpr int IPW = TK * D * 2 / 1024 / NW;
+  if (kr.indexed && key0 + TK <= kr.n_pre) {
+    // a retained-row tile: this wave's indices are read before its DMAs go
+    // out (an index read between two DMAs waits out an LDS round trip)
+    constexpr int ROWB = D * 2;
+    constexpr int CPR = ROWB / 16;
+    constexpr int RPI = 1024 / ROWB;
+    const int32_t* tidx = sidx + (key0 - kbeg);
+    int64_t row[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) row[j] = tidx[(wave * IPW + j) * RPI + lane / CPR];
+    const char* base = isv ? kr.vpre : kr.kpre;
+    const int64_t st = isv ? kr.vp_st : kr.kp_st;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int k = wave * IPW + j;
+      const int r = k * RPI + lane / CPR;
+      const int lc = (lane % CPR) ^ (isv ? swz_v<CPR>(r) : swz_k<CPR>(r));
+      dma_1k(base + row[j] * st + 16 * lc, dst + k * 1024);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < IPW; ++j) dma_one<D, TK>(kr, isv, key0, dst, wave * IPW + j, lane, sidx, kbeg);
 }

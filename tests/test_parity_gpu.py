@@ -96,6 +96,20 @@ def test_full_with_outliers(ba):
     check_full(ba, sh)
 
 
+# Retained rows on the sequential kernel, where every row wave issues its share
+# of each gathered tile: 64, 128 and 256 packed rows per workgroup (2, 4 and 8
+# row waves). More than 8192 keys keep the plan from cutting the rows into
+# one-wave chunks; ragged kept counts end the gathered rows inside a tile.
+@pytest.mark.parametrize("kw", [
+    dict(batch=2, q_heads=8, kv_heads=4, block_len=32, prefix_len=9000, n_keep=8213),   # 64 rows: 2 waves
+    dict(batch=1, q_heads=16, kv_heads=4, block_len=32, prefix_len=9000, n_keep=8250),  # 128 rows: 4 waves
+    dict(batch=1, q_heads=8, kv_heads=1, block_len=32, prefix_len=9000, n_keep=8301),   # 256 rows: 8 waves
+], ids=["rows64", "rows128", "rows256"])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_full_gathered_prefix_sequential_kernel(ba, kw, splits):
+    check_full(ba, datagen.scaled_shape("sparse_gqa", **kw), splits=splits)
+
+
 # More partials than one chunk of the split merge, which folds them 16 at a
 # time and carries the running max and sum from chunk to chunk (the last chunk
 # ragged): forced split counts past 16 for each kernel family, for the final

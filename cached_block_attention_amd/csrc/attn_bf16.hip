@@ -350,13 +350,14 @@ __device__ __forceinline__ void dma_tile_all_pre(const KeyRows& kr, bool isv, in
 
 // This wave's share of the DMA of one K (or V) tile: with NW waves issuing,
 // wave w issues instructions w*IPW .. w*IPW + IPW - 1, in the general form.
-template <int D, int TK, int NW>
+template <int D, int TK, int NW, bool IDX = false>
 __device__ __forceinline__ void dma_tile(const KeyRows& kr, bool isv, int64_t key0, uint32_t dst, int wave,
                                          int lane, const int32_t* sidx, int64_t kbeg) {
   constexpr int IPW = TK * D * 2 / 1024 / NW;
-  if (kr.indexed && key0 + TK <= kr.n_pre) {
-    // a retained-row tile: this wave's indices are read before its DMAs go
-    // out (an index read between two DMAs waits out an LDS round trip)
+  if (IDX && key0 + TK <= kr.n_pre) {
+    // a retained-row tile (IDX: launches with retained-row indices): this
+    // wave's indices are read before its DMAs go out (an index read between
+    // two DMAs waits out an LDS round trip)
     constexpr int ROWB = D * 2;
     constexpr int CPR = ROWB / 16;
     constexpr int RPI = 1024 / ROWB;
@@ -827,7 +828,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 // tile; with DMAW one more wave (wave NW, no rows) issues them all instead, so
 // that a row wave never stalls behind the memory pipeline between its
 // products.
-template <int D, int NW, int TK, int NS, bool DMAW = false, bool NT = false>
+template <int D, int NW, int TK, int NS, bool DMAW = false, bool NT = false, bool IDX = false>
 __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnParams p) {
   constexpr int TB = TK * D * 2;                       // bytes of a K (or V) tile
   constexpr int IPW = DMAW ? TB / 1024 : TB / 1024 / NW;  // DMA instructions per issuing wave per K (or V) tile
@@ -857,8 +858,8 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
       dma_tile_all<D, TK, NT>(s.kr, false, key0, slot, lane, sidx, s.kbeg);
       dma_tile_all<D, TK, NT>(s.kr, true, key0, slot + TB, lane, sidx, s.kbeg);
     } else {
-      dma_tile<D, TK, NW>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
-      dma_tile<D, TK, NW>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
+      dma_tile<D, TK, NW, IDX>(s.kr, false, key0, slot, wave, lane, sidx, s.kbeg);
+      dma_tile<D, TK, NW, IDX>(s.kr, true, key0, slot + TB, wave, lane, sidx, s.kbeg);
     }
   };
 
@@ -1063,8 +1064,12 @@ hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev)
   } else {
     constexpr int TK = NW == 1 ? 32 : 64;
     constexpr int NS = 4;
-    hipExtLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, ev.start, ev.stop, 0,
-                          p);
+    if (p.keys.idx != nullptr)  // retained rows: the gathered form of each wave's DMA share
+      hipExtLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS, false, false, true>), grid, dim3(64 * NW), 0, stream,
+                            ev.start, ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS>), grid, dim3(64 * NW), 0, stream, ev.start, ev.stop,
+                            0, p);
   }
   return hipGetLastError();
 }

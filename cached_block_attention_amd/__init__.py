@@ -237,6 +237,15 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr() if t is not None else None
 
 
+def _retained(idx, n_keep: int, prefix_len: int):
+    """(prefix_len, idx) as the C ABI takes them. An empty retained set is an
+    empty prefix: a zero-element tensor has no device address, and a NULL index
+    array would mean the dense prefix."""
+    if idx is not None and n_keep == 0:
+        return 0, None
+    return prefix_len, idx
+
+
 def _stream(stream) -> Optional[int]:
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -313,7 +322,8 @@ def blkattn_full(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, scale=Non
     _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
     n_keep = _check_idx(idx, B, Hkv)
     _check_gpu(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx)
-    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    P, idx = _retained(idx, n_keep, k_pre.shape[2])
+    dims = make_dims(q, k_pre.shape[1], P, n_keep, scale, splits)
     ws, nbytes = _workspace(dims, OP_FULL, q.device, workspace)
     st = library().blkattn_full(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
                                 _ref(_tensor(v_pre)), _ptr(idx), _ref(_tensor(k_blk)),
@@ -336,7 +346,8 @@ def blkattn_full_noalloc(q, k_pre, v_pre, k_blk, v_blk, o, lse=None, idx=None, s
     _expect(lse, "lse", (B, Hq, Bq), torch.float32, contiguous=True, optional=True)
     n_keep = _check_idx(idx, B, Hkv)
     _check_gpu(q, k_pre, v_pre, k_blk, v_blk, o, lse, idx)
-    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    P, idx = _retained(idx, n_keep, k_pre.shape[2])
+    dims = make_dims(q, k_pre.shape[1], P, n_keep, scale, splits)
     st = library().blkattn_full_noalloc(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
                                         _ref(_tensor(v_pre)), _ptr(idx), _ref(_tensor(k_blk)),
                                         _ref(_tensor(v_blk)), _ref(_tensor(o)), _ptr(lse), _stream(stream))
@@ -351,7 +362,8 @@ def blkattn_prefix_partial(q, k_pre, v_pre, out: Partial, idx=None, scale=None, 
     _check_partial_shape(out, "out", B, Hq, q.shape[2], d)
     n_keep = _check_idx(idx, B, Hkv)
     _check_gpu(q, k_pre, v_pre, idx, *out)
-    dims = make_dims(q, k_pre.shape[1], k_pre.shape[2], n_keep, scale, splits)
+    P, idx = _retained(idx, n_keep, k_pre.shape[2])
+    dims = make_dims(q, k_pre.shape[1], P, n_keep, scale, splits)
     ws, nbytes = _workspace(dims, OP_PREFIX_PARTIAL, q.device, workspace)
     st = library().blkattn_prefix_partial(ctypes.byref(dims), _ref(_tensor(q)), _ref(_tensor(k_pre)),
                                           _ref(_tensor(v_pre)), _ptr(idx), _ref(_partial(out)),
@@ -450,6 +462,8 @@ def blkattn_gather_prefix(k_full, v_full, idx, k_out, v_out, stream=None):
     _expect(k_out, "k_out", (B, Hkv, n, d), k_full.dtype)
     _expect(v_out, "v_out", (B, Hkv, n, d), k_full.dtype)
     _check_gpu(k_full, v_full, idx, k_out, v_out)
+    if n == 0:  # no rows to copy (an empty tensor has no device address to pass)
+        return k_out, v_out
     dims = Dims(B, Hkv, Hkv, d, 1, int(idx.shape[-1]), P, _dtype_code(k_full), 1.0, 0, 0)
     st = library().blkattn_gather_prefix(ctypes.byref(dims), _ref(_tensor(k_full)), _ref(_tensor(v_full)),
                                          _ptr(idx), _ref(_tensor(k_out)), _ref(_tensor(v_out)),
@@ -488,6 +502,8 @@ def blkattn_select_retained(mass, idx, workspace=None, stream=None):
     if n > P:
         raise ValueError(f"idx asks for {n} rows of {P}")
     _check_gpu(mass, idx)
+    if n == 0:  # nothing to select (an empty tensor has no device address to pass)
+        return idx
     dims = Dims(B, Hkv, Hkv, 64, 1, int(idx.shape[-1]), P, F32, 1.0, 0, 0)
     ws, nbytes = _workspace(dims, OP_SELECT, mass.device, workspace)
     st = library().blkattn_select_retained(ctypes.byref(dims), _ptr(mass), _ptr(idx), _ptr(ws), nbytes,

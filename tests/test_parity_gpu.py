@@ -323,6 +323,30 @@ def test_empty_prefix_partial_and_merges(ba):
     assert np.all(down(oe) == 0) and np.all(np.isneginf(down(le)))
 
 
+@pytest.mark.parametrize("kw", [dict(batch=2, q_heads=4, kv_heads=2, prefix_len=63, block_len=1),
+                                dict(batch=1, q_heads=28, kv_heads=4, prefix_len=700, block_len=32)],
+                         ids=["B2-G2x2-P63-Bq1", "B1-G7x4-P700-Bq32"])
+def test_empty_retained_set_is_an_empty_prefix(ba, kw):
+    # n_keep = 0 beside a dense prefix: the keys are the block's alone (an
+    # empty index tensor has no device address; it must not read as "dense")
+    import torch
+    sh = datagen.scaled_shape("sparse_gqa", n_keep=0, **kw)
+    say(f"case empty retained set {sh}")
+    inp = datagen.make_inputs(sh)
+    assert inp.idx is not None and inp.idx.shape[-1] == 0
+    t = upload(inp)
+    o, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], idx=t["idx"])
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"], idx=t["idx"])
+    ko = torch.empty(sh.batch, sh.kv_heads, 0, sh.head_dim, dtype=t["k_pre"].dtype, device="cuda")
+    ba.blkattn_gather_prefix(t["k_pre"], t["v_pre"], t["idx"], ko, ko.clone())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale, idx=inp.idx)
+    eo, el = max_err(down(o), o_ref), max_err(down(lse), lse_ref)
+    say(f"  max err O {eo:.3e} LSE {el:.3e}")
+    assert eo <= TOL[sh.dtype]["o"] and el <= TOL[sh.dtype]["lse"], (eo, el)
+    assert np.all(down(pp.o) == 0) and np.all(np.isneginf(down(pp.m))) and np.all(down(pp.l) == 0)
+
+
 @pytest.mark.parametrize("dtype_name,kw", [("bf16", dict(prefix_len=3000, n_keep=700)),
                                            ("f32", dict(prefix_len=500, n_keep=77))])
 def test_gather_bit_exact(ba, dtype_name, kw):

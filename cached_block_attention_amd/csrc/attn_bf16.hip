@@ -718,7 +718,9 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[D / 16], const AttnParams&
 
 // Empty state, or the initial state from a cached partial (LaCache Appendix J:
 // the running (m, l, O~) of a later step starts from the cache): O~ = l * o,
-// m in base 2, l carried by the lanes of the first wave half.
+// m in base 2, l carried by the lanes of the first wave half. The cached o, m
+// and l are loaded together and the empty-row test is applied afterwards as a
+// select, so that no load waits for another (an empty row's o is ignored).
 template <int D>
 __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p, const RowInfo& s, int lane) {
   const int h = lane >> 5;
@@ -733,22 +735,27 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
   if (p.init_m != nullptr && s.row_ok) {
     const float mi = p.init_m[s.mrow];
     const float li = p.init_l[s.mrow];
-    if (mi > -INFINITY && li > 0.0f) {
+    const float* orow = p.init_o + s.mrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = *(const float4*)(orow + 32 * db + 8 * r4 + 4 * h);
+        st.oacc[db][4 * r4 + 0] = v.x;
+        st.oacc[db][4 * r4 + 1] = v.y;
+        st.oacc[db][4 * r4 + 2] = v.z;
+        st.oacc[db][4 * r4 + 3] = v.w;
+      }
+    const bool live = mi > -INFINITY && li > 0.0f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[db][r] = live ? st.oacc[db][r] * li : 0.0f;
+    if (live) {
       st.m2 = mi * kLog2e;
       st.mtrue = st.m2;
       st.lsum = h == 0 ? li : 0.0f;
       lrow = li;
-      const float* orow = p.init_o + s.mrow * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 v = *(const float4*)(orow + 32 * db + 8 * r4 + 4 * h);
-          st.oacc[db][4 * r4 + 0] = v.x * li;
-          st.oacc[db][4 * r4 + 1] = v.y * li;
-          st.oacc[db][4 * r4 + 2] = v.z * li;
-          st.oacc[db][4 * r4 + 3] = v.w * li;
-        }
     }
   }
   const float lq = for_lsum_lane(lrow, lane);
@@ -841,7 +848,8 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
   const int n = lane & 31;
-  const Setup<D> s = setup<D, TK, NW + DMAW>(p, sidx, wave);
+  // the query and initial-state loads go first, so that their latency
+  // overlaps that of the retained-index staging
   bf16x8_t qf[D / 16];
   RowState<D> st;
   {
@@ -849,6 +857,7 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
     load_q<D>(qf, p, ri, h);
     init_state<D>(st, p, ri, lane);
   }
+  const Setup<D> s = setup<D, TK, NW + DMAW>(p, sidx, wave);
   const uint32_t ring_lds = lds_addr(ring);
   const bool issuer = !DMAW || wave == NW;  // wave-uniform
   auto issue = [&](int t) __attribute__((always_inline)) {
@@ -1048,21 +1057,23 @@ template <int D, int NW>
 hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev) {
   dim3 grid(p.splits, p.kv_heads * p.row_chunks, p.batch);
   const bool nt = p.keys.stream_nt != 0;  // a dense prefix longer than the last-level cache
-  if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
-    if (nt)
-      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
-    else
-      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
-  } else if (NW == 1 && p.tiles >= 4 * p.splits) {
-    // one row wave over a long key range: a second wave issues the DMAs
+  if constexpr (NW == 1) {
+    // one row wave: a second wave issues the DMAs, so that the row wave never
+    // stalls behind the memory pipeline, and so that the first tiles are
+    // requested while the row wave's query and initial state are in flight
     if (nt)
       hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true, true>), grid, dim3(128), 0, stream, ev.start,
                             ev.stop, 0, p);
     else
       hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
                             p);
+  } else if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
+    if (nt)
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+    else
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else {
-    constexpr int TK = NW == 1 ? 32 : 64;
+    constexpr int TK = 64;
     constexpr int NS = 4;
     if (p.keys.idx != nullptr)  // retained rows: the gathered form of each wave's DMA share
       hipExtLaunchKernelGGL((attn_bf16_kernel<D, NW, TK, NS, false, false, true>), grid, dim3(64 * NW), 0, stream,

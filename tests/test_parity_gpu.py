@@ -110,6 +110,16 @@ def test_full_gathered_prefix_sequential_kernel(ba, kw, splits):
     check_full(ba, datagen.scaled_shape("sparse_gqa", **kw), splits=splits)
 
 
+# One row wave and its DMA wave over splits of one to three 32-key tiles of
+# retained rows (the block's keys after them): the first tiles are requested
+# while the row wave's query loads are in flight.
+@pytest.mark.parametrize("n_keep", [1, 40, 95])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_full_few_retained_tiles_one_row_wave(ba, n_keep, splits):
+    check_full(ba, datagen.scaled_shape("llada_bf16", q_heads=4, kv_heads=4, prefix_len=500, n_keep=n_keep),
+               splits=splits)
+
+
 # More partials than one chunk of the split merge, which folds them 16 at a
 # time and carries the running max and sum from chunk to chunk (the last chunk
 # ragged): forced split counts past 16 for each kernel family, for the final
@@ -321,6 +331,33 @@ def test_empty_prefix_partial_and_merges(ba):
     oe, le = ba.merge(pe, pe, dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert np.all(down(oe) == 0) and np.all(np.isneginf(down(le)))
+
+
+def test_block_step_ignores_the_o_of_empty_cached_rows(ba):
+    # rows whose cached state is empty (m = -inf, l = 0) start from nothing,
+    # whatever their cached o holds (NaN here): block-only attention for those
+    # rows, the cached state continued for the others
+    import torch
+    sh = shape(batch=2, q_heads=8, kv_heads=2, prefix_len=600, block_len=32)
+    say(f"case block step over partly empty cached rows {sh}")
+    inp = datagen.make_inputs(sh)
+    t = upload(inp)
+    pp = ba.prefix_partial(t["q"], t["k_pre"], t["v_pre"])
+    dead = np.random.default_rng(7).random(tuple(pp.m.shape)) < 0.3
+    dt = torch.from_numpy(dead).cuda()
+    pp.m[dt] = -float("inf")
+    pp.l[dt] = 0.0
+    pp.o[dt] = float("nan")
+    o, lse = ba.block_step(t["q"], t["k_blk"], t["v_blk"], pp)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.partial(inp.q, inp.k_pre, inp.v_pre, sh.scale)
+    ro[dead], rm[dead], rl[dead] = 0.0, -np.inf, 0.0
+    want_o, _, _, want_lse = oracle.merge((ro, rm, rl), oracle.partial(inp.q, inp.k_blk, inp.v_blk, sh.scale))
+    got_o, got_lse = down(o), down(lse)
+    assert not np.isnan(got_o).any() and not np.isnan(got_lse).any()
+    eo, el = max_err(got_o, want_o), max_err(got_lse, want_lse)
+    say(f"  max err O {eo:.3e} LSE {el:.3e} ({int(dead.sum())} of {dead.size} rows empty)")
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"], (eo, el)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, q_heads=4, kv_heads=2, prefix_len=63, block_len=1),

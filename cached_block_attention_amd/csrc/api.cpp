@@ -38,6 +38,11 @@ constexpr int64_t kMinChunkRows = 32;
 // The MI355X last-level (Infinity) cache.
 constexpr int64_t kLastLevelCacheBytes = (int64_t)256 << 20;
 constexpr int64_t kFineChunkKeys = 8192;
+// Packed rows of one ping-pong workgroup (seven row waves), and the fewest
+// 64-key tiles per workgroup for which that kernel is chosen over finer
+// chunks of a launch that would not fill the GPU.
+constexpr int64_t kPingPongRows = 224;
+constexpr int64_t kPingPongMinTiles = 8;
 constexpr size_t kWsAlign = 256;
 
 int fail(int status, const char* fmt, ...) {
@@ -147,6 +152,27 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
     if (sp < 1) sp = 1;
     pl.splits = (int)sp;
     return pl;
+  }
+  // More packed rows than one ping-pong workgroup holds (225 or more) over a
+  // long key range: chunks of 129 to 224 rows keep the ping-pong kernel, whose
+  // MFMA and softmax phases run at the same time, even when the launch then
+  // holds fewer workgroups than the GPU has compute units. Per 64-key tile and
+  // packed row it costs about a quarter of the sequential four-wave kernel the
+  // halving below would reach (large blocks: Bq 1024 over its own keys).
+  if (R > kPingPongRows) {
+    const int64_t c = (R + kPingPongRows - 1) / kPingPongRows;
+    const int64_t rows = (R + c - 1) / c;
+    if (bf16_waves_for_rows(rows) == 8) {
+      Plan pp;
+      pp.row_chunks = (int)c;
+      pp.waves = 8;
+      pp.rows_per_wg = (int)(32 * ((rows + 31) / 32));
+      pp.tile_keys = bf16_tile_keys(8);
+      pp.tiles = (int)((n_keys + pp.tile_keys - 1) / pp.tile_keys);
+      const int64_t base = (int64_t)d->batch * d->kv_heads * c;
+      pp.splits = (int)plan_splits(d, pp, base, bf16_workgroups_per_cu(8), n_keys, indexed);
+      if (2 * base * pp.splits >= kComputeUnits && pp.tiles >= kPingPongMinTiles * pp.splits) return pp;
+    }
   }
   // Packed-row chunks of at most `cap` rows, one workgroup each per key split.
   // The cap starts at 256 (eight waves); when the launch would still hold

@@ -29,6 +29,10 @@ def ba():
     dict(q_heads=8, kv_heads=2, block_len=300),                  # 1200 packed rows per kv head
     dict(q_heads=2, kv_heads=1, head_dim=64, block_len=1000),
     dict(batch=2, q_heads=2, kv_heads=2, block_len=1024),
+    # 32 heads: enough 224-row chunks for the ping-pong kernel (five per head,
+    # the last one with 128 or 104 rows and idle row waves)
+    dict(q_heads=32, kv_heads=32, block_len=1024),
+    dict(q_heads=32, kv_heads=32, block_len=1000),
 ])
 def test_block_partial_large(ba, kw):
     import torch

@@ -154,11 +154,14 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
     return pl;
   }
   // More packed rows than one ping-pong workgroup holds (225 or more) over a
-  // long key range: chunks of 129 to 224 rows keep the ping-pong kernel, whose
-  // MFMA and softmax phases run at the same time, even when the launch then
-  // holds fewer workgroups than the GPU has compute units. Per 64-key tile and
-  // packed row it costs about a quarter of the sequential four-wave kernel the
+  // long key range, in a launch of at most one workgroup per compute unit:
+  // chunks of 129 to 224 rows keep the ping-pong kernel, whose MFMA and
+  // softmax phases run at the same time, even when the launch then holds
+  // fewer workgroups than the GPU has compute units. Per 64-key tile and
+  // packed row it costs about 40 % of the sequential four-wave kernel the
   // halving below would reach (large blocks: Bq 1024 over its own keys).
+  // Launches of several rounds keep the 256-row chunks of the sequential
+  // eight-wave kernel: 224-row chunks would add a partial round.
   if (R > kPingPongRows) {
     const int64_t c = (R + kPingPongRows - 1) / kPingPongRows;
     const int64_t rows = (R + c - 1) / c;
@@ -171,7 +174,8 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
       pp.tiles = (int)((n_keys + pp.tile_keys - 1) / pp.tile_keys);
       const int64_t base = (int64_t)d->batch * d->kv_heads * c;
       pp.splits = (int)plan_splits(d, pp, base, bf16_workgroups_per_cu(8), n_keys, indexed);
-      if (2 * base * pp.splits >= kComputeUnits && pp.tiles >= kPingPongMinTiles * pp.splits) return pp;
+      const int64_t wgs = base * pp.splits;
+      if (2 * wgs >= kComputeUnits && wgs <= kComputeUnits && pp.tiles >= kPingPongMinTiles * pp.splits) return pp;
     }
   }
   // Packed-row chunks of at most `cap` rows, one workgroup each per key split.

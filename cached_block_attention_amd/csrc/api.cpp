@@ -206,15 +206,24 @@ Plan make_plan(const blkattn_dims* d, int64_t n_keys, bool indexed) {
 
 struct WsLayout {
   size_t o = 0, m = 0, l = 0, total = 0;
+  size_t mls = 0;  // bf16 kernels: {m, l, 1/scale, 0} records (o is fp16); 0 = none (m, l arrays)
 };
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Split partials of one call. bf16 kernels: o [splits][rows][d] fp16 (scaled
+// per row), then one {m, l, 1/scale, 0} fp32 record per (split, row). fp32
+// kernel: o [splits][rows][d] fp32, then m and l [splits][rows] fp32.
 WsLayout ws_layout(const blkattn_dims* d, int splits) {
   WsLayout w;
   if (splits <= 1) return w;
   const size_t rows = (size_t)d->batch * d->q_heads * d->block_len;
   w.o = 0;
+  if (d->dtype == BLKATTN_BF16) {
+    w.mls = align_up((size_t)splits * rows * d->head_dim * 2);
+    w.total = align_up(w.mls + (size_t)splits * rows * 16);
+    return w;
+  }
   w.m = align_up(w.o + (size_t)splits * rows * d->head_dim * sizeof(float));
   w.l = align_up(w.m + (size_t)splits * rows * sizeof(float));
   w.total = align_up(w.l + (size_t)splits * rows * sizeof(float));
@@ -328,8 +337,9 @@ int run_splits(const blkattn_dims* d, AttnParams& p, const Plan& pl, const blkat
   char* ws = (char*)workspace;
   p.out.mode = kOutSplit;
   p.out.po = (float*)(ws + wl.o);
-  p.out.pm = (float*)(ws + wl.m);
-  p.out.pl = (float*)(ws + wl.l);
+  p.out.pm = wl.mls != 0 ? nullptr : (float*)(ws + wl.m);
+  p.out.pl = wl.mls != 0 ? nullptr : (float*)(ws + wl.l);
+  p.out.pmls = wl.mls != 0 ? (float4*)(ws + wl.mls) : nullptr;
   p.out.split_rows = rows;
   if ((st = launch_attn(d, p, pl, s))) return st;
   MergeParams mp{};
@@ -338,6 +348,7 @@ int run_splits(const blkattn_dims* d, AttnParams& p, const Plan& pl, const blkat
   mp.strided = 1;
   mp.split_rows = rows;
   mp.src_o[0] = p.out.po, mp.src_m[0] = p.out.pm, mp.src_l[0] = p.out.pl;
+  mp.src_mls = p.out.pmls;
   mp.out_dtype = d->dtype;
   mp.rows = p.rows;
   if (o != nullptr) {

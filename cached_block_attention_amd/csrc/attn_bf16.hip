@@ -62,6 +62,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
@@ -731,7 +733,6 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
   st.m2 = -INFINITY;
   st.mtrue = -INFINITY;
   st.lsum = 0.0f;
-  float lrow = 0.0f;  // this lane's query's initial sum of the weights
   if (p.init_m != nullptr && s.row_ok) {
     const float mi = p.init_m[s.mrow];
     const float li = p.init_l[s.mrow];
@@ -755,29 +756,63 @@ __device__ __forceinline__ void init_state(RowState<D>& st, const AttnParams& p,
       st.m2 = mi * kLog2e;
       st.mtrue = st.m2;
       st.lsum = h == 0 ? li : 0.0f;
-      lrow = li;
     }
   }
-  const float lq = for_lsum_lane(lrow, lane);
+  // The rounded-weight sum starts at 0; the finish adds the cached l, moved to
+  // the final reference max (init_sum), so that no initial value of it has to
+  // stay alive through the tile loop.
 #pragma unroll
-  for (int r = 0; r < 4; ++r) st.lacc[r] = lq;
+  for (int r = 0; r < 4; ++r) st.lacc[r] = 0.0f;
+}
+
+// The cached l of an initial state, moved from its reference max to the final
+// one m2 (base 2): the rescales of the loop multiplied O~ by the product of
+// exp2(m_old - m_new), which telescopes to exp2(m_init - m2).
+__device__ __forceinline__ float init_sum(const AttnParams& p, const RowInfo& s, float m2) {
+  if (p.init_m == nullptr) return 0.0f;
+  const float mi = p.init_m[s.mrow];
+  const float li = p.init_l[s.mrow];
+  return mi > -INFINITY && li > 0.0f ? li * __builtin_amdgcn_exp2f(mi * kLog2e - m2) : 0.0f;
 }
 
 // Finish: o = O~ / l, L = m + ln l (natural-log units), to the final O + LSE,
-// a caller's partial, or the split workspace.
-template <int D>
+// a caller's partial, or the split workspace. In the split workspace o is
+// stored as fp16 times 2^(14 - k), where the row's largest |o| lies in
+// [2^(k-1), 2^k): that element lands in [2^13, 2^14), below the fp16 range's
+// end whatever the magnitude of V, and every element keeps an error of at
+// most 2^-12 of the row's largest (fp16 rounding), far below the bf16
+// rounding of the merged O. The inverse scale 2^(k - 14) goes with m and l.
+// FM restricts the output modes compiled in (kFinishAny: all three, chosen at
+// run time; kFinishSplit: the split workspace only; kFinishDirect: the final
+// O or a caller's partial), for kernels whose registers cannot hold the code
+// of all three.
+constexpr int kFinishAny = 0, kFinishSplit = 1, kFinishDirect = 2;
+
+template <int D, int FM = kFinishAny>
 __device__ __forceinline__ void finish(const RowState<D>& st, const AttnParams& p, const RowInfo& s, int lane) {
   const int h = lane >> 5;
+  const int mode = FM == kFinishSplit ? (int)kOutSplit : p.out.mode;
+  const bool split = FM != kFinishDirect && mode == kOutSplit;
   const float ltot = pair_sum(st.lsum);
   // the sum of the rounded weights of this lane's query: its own register,
   // or that of lane l ^ 32 (which holds this query's)
   const float lown = st.lacc[0];
   const float lother = other_half(lown, lane);
-  const float lhtot = lsum_lane_is_own(lane) ? lown : lother;
+  const float lhrun = lsum_lane_is_own(lane) ? lown : lother;
+  float omax = 0.0f;  // largest |O~| of the row (both wave halves), split workspace only
+  if (split) {
+    float a = 0.0f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(st.oacc[db][r]));
+    omax = pair_max(a);
+  }
+  if (!s.row_ok) return;
+  const float lhtot = lhrun + init_sum(p, s, st.m2);
   const bool live = ltot > 0.0f;
   const float inv = live ? 1.0f / lhtot : 0.0f;
-  if (!s.row_ok) return;
-  if (p.out.mode == kOutFinal) {
+  if (!split && mode == kOutFinal) {
     uint16_t* orow = (uint16_t*)p.out.o + s.b * p.out.o_sb + s.hq * p.out.o_sh + s.srow * p.out.o_st;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -795,11 +830,33 @@ __device__ __forceinline__ void finish(const RowState<D>& st, const AttnParams& 
       }
     if (p.out.lse != nullptr && h == 0)
       p.out.lse[s.mrow] = live ? (st.m2 + __log2f(ltot)) * kLn2 : -INFINITY;
+  } else if (split) {
+    const int64_t base =
+        (int64_t)blockIdx.x * p.out.split_rows + ((int64_t)s.b * p.q_heads + s.hq) * p.block_len + s.qi;
+    int k = __builtin_amdgcn_frexp_expf(omax * inv);  // the row's largest |o| is in [2^(k-1), 2^k)
+    k = k < -100 ? -100 : k;
+    const float sc = __builtin_ldexpf(inv, 14 - k);
+    uint16_t* orow = (uint16_t*)p.out.po + base * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * db + 8 * r4 + 4 * h;
+        const f32x2_t a = {st.oacc[db][4 * r4 + 0] * sc, st.oacc[db][4 * r4 + 1] * sc};
+        const f32x2_t b = {st.oacc[db][4 * r4 + 2] * sc, st.oacc[db][4 * r4 + 3] * sc};
+        uint2 w;
+        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, f16x2_t));
+        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, f16x2_t));
+        *(uint2*)(orow + d0) = w;
+      }
+    if (h == 0) {
+      // export the exact max: l is re-referenced from m2 to it
+      p.out.pmls[base] = make_float4(live ? st.mtrue * kLn2 : -INFINITY,
+                                     live ? ltot * __builtin_amdgcn_exp2f(st.m2 - st.mtrue) : 0.0f,
+                                     __builtin_ldexpf(1.0f, k - 14), 0.0f);
+    }
   } else {
-    const int64_t base = p.out.mode == kOutSplit
-                             ? (int64_t)blockIdx.x * p.out.split_rows +
-                                   ((int64_t)s.b * p.q_heads + s.hq) * p.block_len + s.qi
-                             : s.mrow;
+    const int64_t base = s.mrow;
     float* orow = p.out.po + base * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -916,7 +973,11 @@ __global__ __launch_bounds__(64 * (NW + DMAW)) void attn_bf16_kernel(const AttnP
 // landed. The wave waits until at most 47 loads are counted before each group
 // of 16 so the count stays in the field's range. No computing wave waits
 // behind the memory pipeline to issue a load.
-template <int D, bool NT = false>
+//
+// SO (the split workspace as output, chosen at launch) compiles in only that
+// finish: a run-time choice among all three would keep values alive through
+// the loop that the 256 VGPRs cannot hold.
+template <int D, bool NT = false, bool SO = false>
 __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
   constexpr int NW = 8;
   constexpr int TK = 64;
@@ -1048,7 +1109,7 @@ __global__ __launch_bounds__(512) void attn_bf16_pp_kernel(const AttnParams p) {
       if (work) m_last();
     }
   }
-  finish<D>(st, p, row_info(p, wave, opaque(lane)), lane);
+  finish<D, SO ? kFinishSplit : kFinishDirect>(st, p, row_info(p, wave, opaque(lane)), lane);
 }
 
 // Launch shapes: NW waves per workgroup (each 32 packed rows), TK keys per
@@ -1068,8 +1129,15 @@ hipError_t launch_d_nw(const AttnParams& p, hipStream_t stream, KernelEvents ev)
       hipExtLaunchKernelGGL((attn_bf16_kernel<D, 1, 32, 4, true>), grid, dim3(128), 0, stream, ev.start, ev.stop, 0,
                             p);
   } else if (NW == 8 && p.rows_per_wg <= 32 * (NW - 1)) {
-    if (nt)
+    const bool so = p.out.mode == kOutSplit;
+    if (nt && so)
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, true, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0,
+                            p);
+    else if (nt)
       hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+    else if (so)
+      hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D, false, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0,
+                            p);
     else
       hipExtLaunchKernelGGL((attn_bf16_pp_kernel<D>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else {

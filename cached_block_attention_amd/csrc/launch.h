@@ -41,6 +41,13 @@ enum OutMode : int32_t {
   kOutSplit = 2,    // workspace partials, packed rows; split s at offset s * split_rows
 };
 
+// In the split workspace of the bf16 kernels, o is stored as fp16 scaled by a
+// power of two per (split, row) so that the row's largest |o| lies in
+// [2^13, 2^14), and m, l and the inverse scale form one 16-byte record per
+// (split, row) ({m, l, 1/scale, 0} at pmls). fp32 kernels store o as fp32 and
+// m, l in arrays of their own.
+
+
 struct OutDesc {
   int32_t mode;
   void* o;                      // final O
@@ -50,6 +57,7 @@ struct OutDesc {
   float* pm;                    // partial m base
   float* pl;                    // partial l base
   int64_t split_rows;           // rows of one split's partial (B*Hq*Bq) in kOutSplit
+  float4* pmls;                 // kOutSplit, bf16 kernels: {m, l, 1/scale, 0} per row (o is fp16 at po)
 };
 
 // Query-row map. Packed row qi of a head reads sequence row
@@ -91,6 +99,7 @@ struct MergeParams {
   const float* src_l[2];
   int32_t strided;            // 1: sources are src_*[0] + s * split_rows
   int64_t split_rows;
+  const float4* src_mls;      // strided sources: {m, l, 1/scale, 0} records (o fp16), or nullptr (o fp32)
   int32_t out_dtype;          // BLKATTN_F32 / BLKATTN_BF16 for o_final
   void* o_final;              // strided O or nullptr
   int64_t o_sb, o_sh, o_st;

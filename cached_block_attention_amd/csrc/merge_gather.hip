@@ -130,36 +130,54 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // array. A thread's loads share one lane offset from a wave-uniform base per
 // split, and the weights are base-2 exponentials of prescaled differences,
 // one v_exp_f32 each, so a split costs a thread about a dozen instructions.
-template <int D, int CH>
+// O16: the partials of the bf16 kernels: o in fp16, and m, l and the inverse
+// o scale (folded into the split's weight) in one 16-byte record per (split,
+// row) at src_mls, one load for the three; else fp32 o and separate m, l.
+template <int D, int CH, bool O16>
 __global__ __launch_bounds__(256) void merge_split_kernel(const MergeParams p) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
+  constexpr int OB = O16 ? 2 : 4;  // bytes per o element
   constexpr float kLog2eF = 1.4426950408889634f;
   const int64_t rows = p.split_rows;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
-  const uint64_t ooff = (uint64_t)row * (4 * D) + 16u * (uint32_t)c4;
+  const uint64_t ooff = (uint64_t)row * (OB * D) + (4u * OB) * (uint32_t)c4;
   const uint64_t roff = 4u * (uint64_t)row;
-  const uint64_t ostride = (uint64_t)p.split_rows * (4 * D);  // bytes from one split to the next
+  const uint64_t ostride = (uint64_t)p.split_rows * (OB * D);  // bytes from one split to the next
   const uint64_t rstride = (uint64_t)p.split_rows * 4;
   const char* obase = (const char*)p.src_o[0];
   const char* mbase = (const char*)p.src_m[0];
   const char* lbase = (const char*)p.src_l[0];
+  const char* mlsbase = (const char*)p.src_mls;
+  const uint64_t mlsoff = 16u * (uint64_t)row;
+  const uint64_t mlsstride = (uint64_t)p.split_rows * 16;
 
   float M = -INFINITY;
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < p.nsrc; s0 += CH) {
-    float ms[CH], ls[CH];
+    float ms[CH], ls[CH], ss[CH];
     float4 os[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       // past the last split: load the last one again (no branch), weight 0 below
       const int s = s0 + i < p.nsrc ? s0 + i : p.nsrc - 1;
-      ms[i] = *(const float*)(mbase + (uint64_t)s * rstride + roff);
-      ls[i] = *(const float*)(lbase + (uint64_t)s * rstride + roff);
-      os[i] = *(const float4*)(obase + (uint64_t)s * ostride + ooff);
+      if constexpr (O16) {
+        const float4 mls = *(const float4*)(mlsbase + (uint64_t)s * mlsstride + mlsoff);
+        ms[i] = mls.x, ls[i] = mls.y, ss[i] = mls.z;
+        const uint2 raw = *(const uint2*)(obase + (uint64_t)s * ostride + ooff);
+        os[i] = make_float4((float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x & 0xffff)),
+                            (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.x >> 16)),
+                            (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y & 0xffff)),
+                            (float)__builtin_bit_cast(_Float16, (uint16_t)(raw.y >> 16)));
+      } else {
+        ms[i] = *(const float*)(mbase + (uint64_t)s * rstride + roff);
+        ls[i] = *(const float*)(lbase + (uint64_t)s * rstride + roff);
+        ss[i] = 1.0f;
+        os[i] = *(const float4*)(obase + (uint64_t)s * ostride + ooff);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i)
@@ -178,10 +196,11 @@ __global__ __launch_bounds__(256) void merge_split_kernel(const MergeParams p) {
     for (int i = 0; i < CH; ++i) {
       const float w = (ms[i] == -INFINITY) ? 0.0f : ls[i] * __builtin_amdgcn_exp2f(fmaf(ms[i], kLog2eF, -mc2));
       L += w;
-      acc.x = fmaf(w, os[i].x, acc.x);
-      acc.y = fmaf(w, os[i].y, acc.y);
-      acc.z = fmaf(w, os[i].z, acc.z);
-      acc.w = fmaf(w, os[i].w, acc.w);
+      const float wo = w * ss[i];
+      acc.x = fmaf(wo, os[i].x, acc.x);
+      acc.y = fmaf(wo, os[i].y, acc.y);
+      acc.z = fmaf(wo, os[i].z, acc.z);
+      acc.w = fmaf(wo, os[i].w, acc.w);
     }
     M = mc;
   }
@@ -233,14 +252,18 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   const bool split_ws = p.strided != 0;
   if (p.head_dim == 128) {
     const int64_t blocks = (rows + 7) / 8;
-    if (split_ws)
-      hipLaunchKernelGGL((merge_split_kernel<128, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (split_ws && p.src_mls != nullptr)
+      hipLaunchKernelGGL((merge_split_kernel<128, 16, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else if (split_ws)
+      hipLaunchKernelGGL((merge_split_kernel<128, 16, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((merge_kernel<128, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else if (p.head_dim == 64) {
     const int64_t blocks = (rows + 15) / 16;
-    if (split_ws)
-      hipLaunchKernelGGL((merge_split_kernel<64, 16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (split_ws && p.src_mls != nullptr)
+      hipLaunchKernelGGL((merge_split_kernel<64, 16, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else if (split_ws)
+      hipLaunchKernelGGL((merge_split_kernel<64, 16, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((merge_kernel<64, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   } else {

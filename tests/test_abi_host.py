@@ -109,7 +109,8 @@ def test_split_plan_is_a_function_of_dims(lib):
     d = dims()
     assert lib.blkattn_plan_splits(ctypes.byref(d), ba.OP_FULL) == 16
     rows = 4 * 28 * 32
-    assert lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL) >= 16 * rows * (128 + 2) * 4
+    # bf16: fp16 o plus a 16-byte {m, l, inverse o scale} record per (split, row)
+    assert lib.blkattn_workspace_bytes(ctypes.byref(d), ba.OP_FULL) >= 16 * rows * (128 * 2 + 16)
     d1 = dims(splits=1)
     assert lib.blkattn_plan_splits(ctypes.byref(d1), ba.OP_FULL) == 1
     assert lib.blkattn_workspace_bytes(ctypes.byref(d1), ba.OP_FULL) == 0

@@ -192,3 +192,28 @@ def test_one_hot_full_size_metric_workload_sampled(ba):
     el = max_err(down(lse), lse_ref, mask)
     say(f"  full-size one-hot: max err O {eo:.3e} LSE {el:.3e}")
     assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+
+
+@pytest.mark.parametrize("kw", SHAPES, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+@pytest.mark.parametrize("v_scale", [2.0 ** 20, 2.0 ** -30])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_value_magnitudes_outside_fp16(ba, kw, v_scale, splits):
+    """V far beyond fp16's range (|V| up to ~2^23) and far below its normal
+    range (~2^-30): the bf16 kernels keep split partials of o in fp16 scaled by
+    a power of two per row, so O must still match the oracle to the bf16
+    tolerance relative to the size of V (O scales with V, LSE does not)."""
+    import torch
+    sh = datagen.scaled_shape("dream_gqa", **kw)
+    say(f"case value scale 2^{np.log2(v_scale):.0f} {sh} splits={splits}")
+    inp = datagen.make_inputs(sh)
+    inp.v_pre = bf(datagen.bf16_bits_to_f32(inp.v_pre) * np.float32(v_scale))
+    inp.v_blk = bf(datagen.bf16_bits_to_f32(inp.v_blk) * np.float32(v_scale))
+    t = {k: up(getattr(inp, k)) for k in ("q", "k_pre", "v_pre", "k_blk", "v_blk")}
+    o, lse = ba.attention(t["q"], t["k_pre"], t["v_pre"], t["k_blk"], t["v_blk"], splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.full(inp.q, inp.k_pre, inp.v_pre, inp.k_blk, inp.v_blk, sh.scale)
+    eo = max_err(down(o) / v_scale, o_ref / v_scale)
+    el = max_err(down(lse), lse_ref)
+    say(f"  max err O/scale {eo:.3e} LSE {el:.3e}")
+    assert np.all(np.isfinite(down(o)))
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"], (eo, el)

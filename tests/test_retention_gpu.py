@@ -135,11 +135,13 @@ def test_selection_ties_and_edges(ba):
     assert np.array_equal(idx.cpu().numpy(), oracle.select_retained(big.astype(np.float64), 8192))
 
 
-@pytest.mark.parametrize("groups,P,k", [(8, 131072, 8192), (3, 70001, 33333), (1, 1023, 500), (5, 300, 7)])
+@pytest.mark.parametrize("groups,P,k", [(8, 131072, 8192), (3, 70001, 33333), (1, 1023, 500), (5, 300, 7),
+                                         (2, 300007, 20000), (1, 262145, 65536)])
 def test_selection_ties_across_chunks(ba, groups, P, k):
     """Rows equal to the k-th largest mass spread over every workgroup's chunk,
     so the lower-index tie rule is decided across chunk boundaries; the rows
-    are not a multiple of the chunk or of a workgroup."""
+    are not a multiple of the chunk or of a workgroup (the last two cases: more
+    than 2^18 rows per group, 32 chunks of more than 8192 rows each)."""
     import torch
     rng = np.random.default_rng(groups * 1000 + k)
     m = np.full((1, groups, P), 0.5, dtype=np.float32)

@@ -194,7 +194,9 @@ def test_one_hot_full_size_metric_workload_sampled(ba):
     assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
 
 
-@pytest.mark.parametrize("kw", SHAPES, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+@pytest.mark.parametrize("kw", SHAPES + [dict(batch=1, q_heads=14, kv_heads=2, prefix_len=900, block_len=32,
+                                              head_dim=64)],
+                         ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
 @pytest.mark.parametrize("v_scale", [2.0 ** 20, 2.0 ** -30])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_value_magnitudes_outside_fp16(ba, kw, v_scale, splits):

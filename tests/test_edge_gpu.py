@@ -195,7 +195,11 @@ def test_one_hot_full_size_metric_workload_sampled(ba):
 
 
 @pytest.mark.parametrize("kw", SHAPES + [dict(batch=1, q_heads=14, kv_heads=2, prefix_len=900, block_len=32,
-                                              head_dim=64)],
+                                              head_dim=64),
+                                         # 2048 query rows: the merge's eight-values-per-thread form, d 64 and 128
+                                         dict(batch=2, q_heads=32, kv_heads=4, prefix_len=600, block_len=32,
+                                              head_dim=64),
+                                         dict(batch=2, q_heads=32, kv_heads=4, prefix_len=600, block_len=32)],
                          ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
 @pytest.mark.parametrize("v_scale", [2.0 ** 20, 2.0 ** -30])
 @pytest.mark.parametrize("splits", [0, 3])

@@ -54,6 +54,9 @@ def test_block_partial_large(ba, kw):
     (dict(q_heads=4, kv_heads=4, block_len=512, prefix_len=1000), 0),
     (dict(q_heads=14, kv_heads=2, block_len=200, prefix_len=777), 3),
     (dict(dtype=datagen.F32, head_dim=64, q_heads=2, kv_heads=2, block_len=300, prefix_len=250), 2),
+    # 7 q-heads x 256 queries = 1792 packed rows per kv head over 4256 keys: eight 224-row
+    # ping-pong chunks x 8 key splits (256 workgroups), merged from fp16 partials
+    (dict(q_heads=28, kv_heads=4, block_len=256, prefix_len=4000), 0),
 ])
 def test_full_with_large_block(ba, kw, splits):
     import torch

@@ -122,6 +122,11 @@ def test_split_plan_is_a_function_of_dims(lib):
     assert lib.blkattn_plan_splits(ctypes.byref(tiny1), ba.OP_FULL) == 2
     huge = dims(splits=100000)
     assert lib.blkattn_plan_splits(ctypes.byref(huge), ba.OP_FULL) == (32768 + 32 + 63) // 64
+    # more packed rows than one ping-pong workgroup over a long key range, in one round:
+    # 1792 rows per kv head (7 x 256) go in eight 224-row chunks, and 8 key splits fill the
+    # 256 compute units (256-row chunks of the sequential kernel would take 10 splits)
+    big_block = dims(batch=1, block_len=256, prefix_len=4000)
+    assert lib.blkattn_plan_splits(ctypes.byref(big_block), ba.OP_FULL) == 8
     # an indexed prefix stages at most 2048 indices per split
     sparse = dims(batch=2, prefix_len=131072, n_keep=100000, block_len=64, splits=1)
     assert lib.blkattn_plan_splits(ctypes.byref(sparse), ba.OP_FULL) >= (100000 + 64) // 2048
